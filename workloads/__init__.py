@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the tests, the bench and the smoke check; it holds
+no arithmetic of the method (no scores, softmax or products), only the
+recipes that draw Q, K and V.  Both the HIP path and the CPU oracle consume
+exactly the tensors returned here.
+
+Recipe (all workloads): a CPU ``torch.Generator`` seeded with ``seed`` draws
+float32 standard normals in the order Q, K, V, each of shape [B, H, N, d];
+the stress workload then draws one offset per query row.  The float32 values
+are cast to the workload's dtype with round-to-nearest-even, and the oracle
+upcasts those rounded values exactly to float64.
+
+The pages benchmark on synthetic inputs only (a sweep over sequence lengths),
+so no dataset is stood in for.
+"""
+
+from dataclasses import dataclass
+import math
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "fp32" or "bf16"
+    causal: bool
+    stress: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    def describe(self) -> str:
+        mask = "causal" if self.causal else "non-causal"
+        extra = ", stress logits" if self.stress else ""
+        return (f"{self.name}: B={self.B} H={self.H} N={self.N} d={self.d} "
+                f"{self.dtype} {mask}{extra}")
+
+
+# The five workloads: a tiny fp32 case, multi-head bf16, causal bf16 at
+# N=4096/d=128, a long sequence, and a numerical-stress case.
+TINY_FP32 = Workload("tiny_fp32_b1h1n256d64", 1, 1, 256, 64, "fp32", False)
+MULTIHEAD = Workload("mha_bf16_b4h16n1024d64", 4, 16, 1024, 64, "bf16", False)
+CAUSAL_4K = Workload("causal_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf16", True)
+LONG_16K = Workload("long_bf16_b1h16n16384d128", 1, 16, 16384, 128, "bf16", False)
+STRESS = Workload("stress_bf16_b16h16n2048d64", 16, 16, 2048, 64, "bf16", False,
+                  stress=True)
+
+ALL = (TINY_FP32, MULTIHEAD, CAUSAL_4K, LONG_16K, STRESS)
+BY_NAME = {w.name: w for w in ALL}
+
+# The stress workload: Q and K drawn with standard deviation 3, and a per-row
+# offset c ~ U(-20, 20) added to every component of the *scaled* query, i.e.
+# Q <- Q + c / scale before rounding, so that logits reach several hundred.
+STRESS_SD = 3.0
+STRESS_OFFSET = 20.0
+
+
+def make_inputs(w: Workload, seed: int, device="cpu"):
+    """(q, k, v) for workload ``w`` drawn from ``seed``, in w's dtype."""
+    return make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed,
+                    stress=w.stress, scale=w.scale, device=device)
+
+
+def make_qkv(B, H, N, d, dtype, seed, stress=False, scale=None, device="cpu"):
+    """Seeded Q, K, V of shape [B, H, N, d]; see the module docstring."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if stress:
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        q.mul_(STRESS_SD)
+        k.mul_(STRESS_SD)
+        c = torch.rand((B, H, N, 1), generator=g, dtype=torch.float32)
+        c = c.mul_(2.0 * STRESS_OFFSET).sub_(STRESS_OFFSET)
+        q.add_(c / scale)
+    q, k, v = (t.to(dtype) for t in (q, k, v))
+    if device != "cpu":
+        q, k, v = (t.to(device) for t in (q, k, v))
+    return q, k, v
+
+
+def to_f64_numpy(t):
+    """Exact float64 copy of a (CPU or device) tensor for the oracle."""
+    return t.detach().to("cpu", torch.float32).double().numpy()
