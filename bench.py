@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Throughput of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+One step is one fa_fwd call (the whole forward: QK^T, online softmax, PV,
+normalisation, O and L written) over one batch of seeded synthetic inputs
+already resident in device memory.  The default workload is the causal bf16
+case B=2, H=32, N=4096, d=128, on which the MFMA-peak target is stated.
+
+Prints ONE JSON line.  `value` is attention TFLOP/s with the conventional
+count 4*B*H*N^2*d (halved for causal) over the timed steps' wall time.
+`roofline` relates the kernel's average launch duration (HIP events on the
+launch stream) to the dense bf16 MFMA peak.  `cpu_baseline` times the float64
+CPU oracle on a bounded sample of the same workload (whole heads, ~10 s).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) + % of bf16 MFMA peak, 1×MI355X"
+# Dense bf16 MFMA peak of MI355X: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_F32_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "io_aware_softmax_06_amd", "csrc")
+
+
+def attention_flops(w):
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2.0 if w.causal else f
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed PMC summary, if it is current.
+
+    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each
+    scaled by the copy-kernel calibration factor) and the digest of the kernel
+    sources it was taken with; a changed kernel makes the figure stale (None).
+    """
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        m = re.match(r"^(\w+):\s*(\S+)", line)
+        if m:
+            fields[m.group(1)] = m.group(2)
+    if fields.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seed, budget_s=10.0):
+    """The float64 oracle on whole heads of the same inputs, ~budget_s seconds."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs, to_f64_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q, k, v = make_inputs(w, seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]), to_f64_numpy(v[sl]),
+                         w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = attention_flops(w) / (w.B * w.H)
+    del np
+    return {
+        "value": round(per_head * done / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, seed {seed}, "
+                  f"float64 NumPy oracle with materialised S, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward pass is benchmarked on a single "
+              "MI355X (no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_softmax_06_amd as fa
+    import workloads
+
+    fa.load()
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_inputs(w, args.seed, device=dev)
+    O = torch.empty_like(q)
+    L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    flops = attention_flops(w)
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    props = torch.cuda.get_device_properties(dev)
+    print(f"device: {props.name}, {props.multi_processor_count} CUs; kernel avg "
+          f"{avg_launch_s * 1e6:.1f} us (min {min(launch_ms) * 1e3:.1f} us), "
+          f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q, K, V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "dtype": w.dtype, "layout": "[B,H,N,d]",
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

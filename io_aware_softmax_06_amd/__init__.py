@@ -1,0 +1,129 @@
+"""Python binding of libfa355, the gfx950 attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa355.so``.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+
+Raw C-ABI functions (same names and argument order as include/fa355.h):
+    fa_fwd(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype) -> int
+    fa_strerror(status) -> str
+    fa_version() -> int
+where Q, K, V, O, L and stream are integer addresses.
+
+Tensor front end:
+    fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (O, L)
+"""
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa355.so")
+
+FA_BF16 = 0
+FA_F32 = 1
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_UNSUPPORTED_D = -3
+FA_ERR_DTYPE = -4
+FA_ERR_SCALE = -5
+FA_ERR_ALIGN = -6
+FA_ERR_ALIAS = -7
+FA_ERR_HIP = -8
+FA_ERR_ARG = -9
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero status returned by libfa355."""
+
+    def __init__(self, status):
+        super().__init__(f"fa_fwd failed ({status}): {fa_strerror(status)}")
+        self.status = status
+
+
+def load(path=LIB_PATH):
+    """Load libfa355.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m io_aware_softmax_06_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                           ctypes.c_float, ctypes.c_int, vp, ctypes.c_int]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_strerror.argtypes = [ctypes.c_int]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def fa_fwd(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype):
+    """Direct call of the C entry point; returns its status code."""
+    return load().fa_fwd(Q, K, V, O, L, B, H, N, d, float(scale), int(causal), stream, dtype)
+
+
+def fa_strerror(status):
+    return load().fa_strerror(int(status)).decode()
+
+
+def fa_version():
+    return load().fa_version()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward on [B, H, N, d] device tensors; returns (O, L).
+
+    O has q's dtype and shape; L is float32 [B, H, N].  Runs on ``stream``
+    (default: torch's current stream) and does not synchronise.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k and v must share shape, dtype and device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse

@@ -1,0 +1,69 @@
+"""Build libfa355.so in-tree for gfx950 with hipcc.
+
+    python -m io_aware_softmax_06_amd.build [--verbose]
+
+Always recompiles.  The library holds the HIP kernels and the C ABI of
+include/fa355.h; the Python binding in this package loads it with ctypes.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libfa355.so")
+SOURCES = [os.path.join(CSRC, "fa355.hip")]
+DEPENDS = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, "fa355.h")]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # packed-fp32 VALU forms are kept out of the generated code entirely
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc_path():
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libfa355)")
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile libfa355.so; returns its path.  Raises on a compiler error."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc_path(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
+           *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; drop that note.
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def is_stale():
+    """True if the library is missing or older than one of its sources."""
+    if not os.path.exists(LIB_PATH):
+        return True
+    t = os.path.getmtime(LIB_PATH)
+    return any(os.path.getmtime(p) > t for p in DEPENDS if os.path.exists(p))
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

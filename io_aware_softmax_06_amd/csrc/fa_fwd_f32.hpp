@@ -1,0 +1,120 @@
+// Attention forward in float32 end to end (inputs, arithmetic, output).
+//
+// The same one-pass recurrence as the bf16 kernel (wmrh.cn FlashAttention
+// article, section 2.2), on the vector ALU: one wave per workgroup, one query
+// row per lane (two lanes per row when d = 128, each holding 64 of the d
+// components), 32-key tiles of K and V staged in LDS and read as broadcasts.
+// This is the exact-precision variant; bf16 inputs take the MFMA kernel.
+#pragma once
+
+#include "fa_common.hpp"
+
+namespace fa355 {
+
+constexpr int kF32Keys = 32;  // keys per staged tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ Lse, int N, int num_qtiles, float scale,
+    float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int kLanesPerRow = D / 64;
+  constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
+  constexpr int kDl = 64;                   // components of d held per lane
+  __shared__ f32x4 ks[kF32Keys][D / 4];
+  __shared__ f32x4 vs[kF32Keys][D / 4];
+
+  const int lane = threadIdx.x;
+  const int part = lane / kRows;  // which 64 components of d (0 when d = 64)
+  const int bh = blockIdx.x / num_qtiles;
+  int qt = blockIdx.x - bh * num_qtiles;
+  if (CAUSAL) qt = num_qtiles - 1 - qt;
+  const int q0 = qt * kRows;
+  const int qrow = q0 + lane % kRows;
+  const size_t head = (size_t)bh * N * D;
+
+  f32x4 q[kDl / 4], o[kDl / 4];
+#pragma unroll
+  for (int t = 0; t < kDl / 4; ++t) {
+    q[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (qrow < N)
+      q[t] = *reinterpret_cast<const f32x4*>(Q + head + (size_t)qrow * D + part * kDl + 4 * t);
+  }
+  // m_run: largest raw score so far; base_run = fl(m_run * scale_log2), the
+  // base-2 reference of l_run and o (-inf until a visible key is seen), kept
+  // rounded so that exp2(base_old - base_new) rescales exactly.
+  float m_run = kNegInf, base_run = kNegInf, l_run = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += kF32Keys) {
+    __syncthreads();
+    for (int c = lane; c < kF32Keys * (D / 4); c += 64) {
+      const int row = c / (D / 4), col = c % (D / 4);
+      const int key = kv0 + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        kv = *reinterpret_cast<const f32x4*>(K + head + (size_t)key * D + 4 * col);
+        vv = *reinterpret_cast<const f32x4*>(V + head + (size_t)key * D + 4 * col);
+      }
+      ks[row][col] = kv;
+      vs[row][col] = vv;
+    }
+    __syncthreads();
+
+    float s[kF32Keys];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kF32Keys; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < kDl / 4; ++t) {
+        const f32x4 kk = ks[j][part * (kDl / 4) + t];
+        acc = __builtin_fmaf(q[t][0], kk[0], acc);
+        acc = __builtin_fmaf(q[t][1], kk[1], acc);
+        acc = __builtin_fmaf(q[t][2], kk[2], acc);
+        acc = __builtin_fmaf(q[t][3], kk[3], acc);
+      }
+      if (kLanesPerRow == 2) acc += other_half(acc);
+      const int key = kv0 + j;
+      s[j] = (key >= N || (CAUSAL && key > qrow)) ? kNegInf : acc;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float base = (m_new == kNegInf) ? 0.f : m_new * scale_log2;
+    const float alpha = fast_exp2(base_run - base);
+    base_run = (m_new == kNegInf) ? kNegInf : base;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < kDl / 4; ++t) o[t] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kF32Keys; ++j) {
+      const float p = fast_exp2(__builtin_fmaf(s[j], scale_log2, -base));
+      l_run += p;
+#pragma unroll
+      for (int t = 0; t < kDl / 4; ++t) {
+        const f32x4 vv = vs[j][part * (kDl / 4) + t];
+        o[t][0] = __builtin_fmaf(p, vv[0], o[t][0]);
+        o[t][1] = __builtin_fmaf(p, vv[1], o[t][1]);
+        o[t][2] = __builtin_fmaf(p, vv[2], o[t][2]);
+        o[t][3] = __builtin_fmaf(p, vv[3], o[t][3]);
+      }
+    }
+    m_run = m_new;
+  }
+
+  if (qrow < N) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int t = 0; t < kDl / 4; ++t)
+      *reinterpret_cast<f32x4*>(O + head + (size_t)qrow * D + part * kDl + 4 * t) = o[t] * inv;
+    if (part == 0) {
+      const float r = __builtin_fmaf(m_run, scale_log2, -base_run);  // exact residual
+      Lse[(size_t)bh * N + qrow] =
+          l_run > 0.f ? __builtin_fmaf(m_run, scale, logf(l_run) - r * kLn2) : kNegInf;
+    }
+  }
+}
+
+}  // namespace fa355
