@@ -29,7 +29,8 @@ void launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
   const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
   const int total = (int)(BH * num_qtiles);
   hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(fa355::kThreads),
-                     0, stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     fa355::Bf16Layout<D>::kBytes, stream, static_cast<const uint16_t*>(Q),
+                     static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), L, (int)N,
                      num_qtiles, total, scale, scale * fa355::kLog2e);
 }
