@@ -114,6 +114,10 @@ def main():
     ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one elementwise copy of this many MiB "
+                         "(read once, written once) so that a counter run can scale its HBM "
+                         "byte counters against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -152,6 +156,15 @@ def main():
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # one streaming kernel: n*4 bytes read, n*4 written
+        torch.cuda.synchronize()
+        del src, dst
 
     flops = attention_flops(w)
     ms_per_step = wall / args.steps * 1e3
