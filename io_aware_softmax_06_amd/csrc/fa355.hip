@@ -23,20 +23,33 @@ bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
+// instance's limit once per process (device-independent attribute).
 template <int D, bool CAUSAL>
-void launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
-                 int64_t N, float scale, hipStream_t stream) {
+hipError_t prepare_bf16() {
+  static const hipError_t status = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::Bf16Layout<D>::kBytes);
+  return status;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
+                       int64_t BH, int64_t N, float scale, hipStream_t stream) {
+  const hipError_t prep = prepare_bf16<D, CAUSAL>();
+  if (prep != hipSuccess) return prep;
   const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
   const int total = (int)(BH * num_qtiles);
   hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(fa355::kThreads),
                      fa355::Bf16Layout<D>::kBytes, stream, static_cast<const uint16_t*>(Q),
-                     static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), L, (int)N,
-                     num_qtiles, total, scale, scale * fa355::kLog2e);
+                     static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                     static_cast<uint16_t*>(O), L, (int)N, (int)BH, num_qtiles, scale,
+                     scale * fa355::kLog2e);
+  return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-void launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
+hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
                 int64_t N, float scale, hipStream_t stream) {
   constexpr int kRows = 64 / (D / 64);
   const int num_qtiles = (int)((N + kRows - 1) / kRows);
@@ -45,6 +58,7 @@ void launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, 
                      static_cast<const float*>(Q), static_cast<const float*>(K),
                      static_cast<const float*>(V), static_cast<float*>(O), L, (int)N, num_qtiles,
                      scale, scale * fa355::kLog2e);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -84,22 +98,23 @@ extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, floa
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
+  hipError_t err;
   if (dtype == FA_BF16) {
     if (d == 64)
-      causal ? launch_bf16<64, true>(Q, K, V, O, L, BH, N, scale, s)
-             : launch_bf16<64, false>(Q, K, V, O, L, BH, N, scale, s);
+      err = causal ? launch_bf16<64, true>(Q, K, V, O, L, BH, N, scale, s)
+                   : launch_bf16<64, false>(Q, K, V, O, L, BH, N, scale, s);
     else
-      causal ? launch_bf16<128, true>(Q, K, V, O, L, BH, N, scale, s)
-             : launch_bf16<128, false>(Q, K, V, O, L, BH, N, scale, s);
+      err = causal ? launch_bf16<128, true>(Q, K, V, O, L, BH, N, scale, s)
+                   : launch_bf16<128, false>(Q, K, V, O, L, BH, N, scale, s);
   } else {
     if (d == 64)
-      causal ? launch_f32<64, true>(Q, K, V, O, L, BH, N, scale, s)
-             : launch_f32<64, false>(Q, K, V, O, L, BH, N, scale, s);
+      err = causal ? launch_f32<64, true>(Q, K, V, O, L, BH, N, scale, s)
+                   : launch_f32<64, false>(Q, K, V, O, L, BH, N, scale, s);
     else
-      causal ? launch_f32<128, true>(Q, K, V, O, L, BH, N, scale, s)
-             : launch_f32<128, false>(Q, K, V, O, L, BH, N, scale, s);
+      err = causal ? launch_f32<128, true>(Q, K, V, O, L, BH, N, scale, s)
+                   : launch_f32<128, false>(Q, K, V, O, L, BH, N, scale, s);
   }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" const char* fa_strerror(int status) {

@@ -15,18 +15,22 @@
 //    K/V byte fetched from L2 serves 256 rows.
 //  * Scores are produced transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane owns one query column, so a row's
-//    maximum and sum are in-lane reductions plus one half-wave exchange.
+//    maximum and sum are in-lane reductions plus one half-wave exchange
+//    (v_permlane32_swap).
 //  * The output is accumulated transposed too, O^T += V^T P^T, with P^T going
 //    from the score accumulator into the MFMA B operand in registers; the 32
 //    A-operand rows of the score MFMA are mapped to keys by `key_of_row` so
 //    that each half-wave holds 8 consecutive keys per 16-key step.
-//  * K tiles go from global memory straight into LDS (global_load_lds_dwordx4,
-//    no registers), row-major with XOR-swizzled 16-byte chunks.  V tiles go
-//    through registers one tile ahead, are transposed in 4x4 blocks with
-//    v_perm_b32 and stored as V^T ([d][key]), also swizzled; both are read
-//    with conflict-free ds_read_b128.  Both are double-buffered with a single
-//    barrier per tile, and K runs one tile ahead of V so that the score MFMAs
-//    of tile j+1 are issued before the softmax of tile j.
+//  * K and V tiles go from global memory straight into LDS
+//    (global_load_lds_dwordx4, no registers), row-major with XOR-swizzled
+//    16-byte chunks, in a ring of three buffers each: K is fetched three tiles
+//    ahead of its use and V two, so a load has two loop iterations to land.
+//    K rows are read as MFMA A operands with ds_read_b128; V^T operands come
+//    from the row-major V tile through ds_read_b64_tr_b16, whose 16-lane
+//    transpose turns four 8-byte row pieces into one column fragment.
+//  * Per iteration a wave runs two interleaved streams: the score MFMAs of
+//    tile j+1 under the softmax VALU work of tile j, then the P V MFMAs of
+//    tile j under the issue of the next loads.  One barrier per tile.
 //  * The reference point of the online softmax moves only when a row's maximum
 //    grows by more than 2^8 (in base-2 units); until then probabilities are
 //    taken against the stale reference and are at most 2^8, which fp32 and
@@ -44,29 +48,34 @@ constexpr int kBM = 256;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 3;     // ring depth of the K and V tile buffers
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
 
 template <int D>
 struct Bf16Layout {
-  static constexpr int kTileBytes = kBN * D * 2;      // one K tile or one V^T tile
-  static constexpr int kOffK0 = 0;
-  static constexpr int kOffK1 = kTileBytes;
-  static constexpr int kOffV0 = 2 * kTileBytes;
-  static constexpr int kOffV1 = 3 * kTileBytes;
-  static constexpr int kBytes = 4 * kTileBytes;       // 64 KB at d = 128
-  static constexpr int kRowBytesK = 2 * D;            // K row: D bf16
-  static constexpr int kRowBytesV = 2 * kBN;          // V^T row: kBN bf16
-  static constexpr int kKLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
+  static constexpr int kTileBytes = kBN * D * 2;      // one K or V tile
+  static constexpr int kRowBytes = 2 * D;             // one K or V row
+  static constexpr int kOffK = 0;                     // kStages K tiles
+  static constexpr int kOffV = kStages * kTileBytes;  // kStages V tiles
+  static constexpr int kBytes = 2 * kStages * kTileBytes;  // 96 KB at d = 128
+  static constexpr int kLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
+  static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
+  static_assert(kLoadsPerWave >= 1 && kLoadsPerTile % kWaves == 0, "tile split over waves");
 };
 
-// 16-byte chunk swizzles (chunk index XOR a function of the row) that keep
-// both the writes and the MFMA-operand reads of a tile free of LDS bank
-// conflicts.  K rows are 2D bytes; V^T rows are 128 bytes.
+// 16-byte chunk swizzles (chunk index XOR a function of the row).  K: keeps the
+// ds_read_b128 operand reads (32 rows x 2 chunks per instruction) conflict
+// free.  V: the transpose reads of one instruction touch 8 rows {r0..r0+3,
+// r0+8..r0+11} x 4 chunks; XOR-ing the chunk's upper bits with the row spreads
+// them evenly over the banks.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 1) & 7) ^ ((d >> 4) & 1); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 // Key (within a 32-key block) fed to A-operand row i of the score MFMA.  With
 // i = 8g + 4h + r (g = 0..3, h = 0..1, r = 0..3) the accumulator element
@@ -81,26 +90,58 @@ __device__ __forceinline__ bf16x8 lds_bf16x8(const char* smem, int byte_off) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + byte_off));
 }
 
-// Direct global->LDS copy of one K tile.  Each wave issues kKLoadsPerTile/8
-// instructions; lane i of an instruction fills physical bytes [16i, 16i+16) of
-// its 1 KB slice, so it fetches the logical chunk that the swizzle puts there.
-// Rows past N are clamped to row N-1: their scores are masked anyway.
-template <int D>
-__device__ __forceinline__ void load_k_tile_direct(char* smem, int buf_off,
-                                                   const uint16_t* __restrict__ Kb, int kv0,
-                                                   int N, int wave, int lane) {
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element (i % 4) of the 8-byte pieces that lanes 4e + i/4 point
+// at, e = 0..3.  Issued from inline asm: the compiler would otherwise wait for
+// every outstanding direct-to-LDS load before it, which defeats the prefetch.
+// The caller waits for the result with lds_wait<N>() and pins it with pin().
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t lds_addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// Orders every later use of v after the preceding lds_wait (asm statements
+// keep their relative order; the use depends on this one's output).
+__device__ __forceinline__ void pin(u32x2& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ uint32_t lds_address(const char* p) {
+  // generic -> LDS address-space cast; the LDS pointer's value is the offset
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// implied vmcnt(0) would also wait for the loads that are meant to stay in
+// flight across it.  The callers wait for exactly the loads they need first.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global->LDS copy of one K or V tile (swizzled rows).  Each wave
+// issues kLoadsPerWave instructions; lane i of an instruction fills physical
+// bytes [16i, 16i+16) of its 1 KB slice, so it fetches the logical chunk that
+// the swizzle puts there.  Rows past N are clamped to row N-1: their scores
+// are masked and their probabilities are 0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
+                                                 const uint16_t* __restrict__ src_head, int kv0,
+                                                 int N, int wave, int lane) {
   using Lay = Bf16Layout<D>;
-  constexpr int kPerWave = Lay::kKLoadsPerTile / kWaves;
-  static_assert(kPerWave >= 1 && Lay::kKLoadsPerTile % kWaves == 0, "K tile split");
 #pragma unroll
-  for (int r = 0; r < kPerWave; ++r) {
-    const int slice = wave * kPerWave + r;
+  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
+    const int slice = wave * Lay::kLoadsPerWave + r;
     const int phys = slice * 1024 + 16 * lane;
-    const int row = phys / Lay::kRowBytesK;
-    const int pch = (phys % Lay::kRowBytesK) / 16;
-    const int ch = pch ^ k_swizzle<D>(row);
+    const int row = phys / Lay::kRowBytes;
+    const int pch = (phys % Lay::kRowBytes) / 16;
+    const int ch = pch ^ (IS_V ? v_swizzle<D>(row) : k_swizzle<D>(row));
     const int key = min(kv0 + row, N - 1);
-    const uint16_t* src = Kb + (size_t)key * D + 8 * ch;
+    const uint16_t* src = src_head + (size_t)key * D + 8 * ch;
     __builtin_amdgcn_global_load_lds(
         reinterpret_cast<__attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(src)),
         reinterpret_cast<__attribute__((address_space(3))) void*>(
@@ -109,73 +150,125 @@ __device__ __forceinline__ void load_k_tile_direct(char* smem, int buf_off,
   }
 }
 
-// V tile staging through registers: each thread owns 4-key x 4-d blocks.
-template <int D>
-struct VStage {
-  static constexpr int kBlocks = (kBN / 4) * (D / 4);
-  static constexpr int kPerThread = (kBlocks + kThreads - 1) / kThreads;
-  u32x2 r[kPerThread][4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_v_tile(VStage<D>& st, const uint16_t* __restrict__ Vb,
-                                            int kv0, int N, int tid) {
-#pragma unroll
-  for (int b = 0; b < VStage<D>::kPerThread; ++b) {
-    const int blk = tid + b * kThreads;
-    if (VStage<D>::kBlocks % kThreads != 0 && blk >= VStage<D>::kBlocks) break;
-    const int dq = blk % (D / 4), kq = blk / (D / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = min(kv0 + 4 * kq + j, N - 1);  // clamped rows get probability 0
-      st.r[b][j] = *reinterpret_cast<const u32x2*>(Vb + (size_t)key * D + 4 * dq);
-    }
-  }
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their
+// maxima).  gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-template <int D>
-__device__ __forceinline__ void store_vt_tile(char* smem, int buf_off, const VStage<D>& st,
-                                              int tid) {
-#pragma unroll
-  for (int b = 0; b < VStage<D>::kPerThread; ++b) {
-    const int blk = tid + b * kThreads;
-    if (VStage<D>::kBlocks % kThreads != 0 && blk >= VStage<D>::kBlocks) break;
-    const int dq = blk % (D / 4), kq = blk / (D / 4);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // keys 4kq..4kq+3 of component d = 4dq + c, packed two per dword
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      const int w = c >> 1;
-      const u32x2 out = {__builtin_amdgcn_perm(st.r[b][1][w], st.r[b][0][w], sel),
-                         __builtin_amdgcn_perm(st.r[b][3][w], st.r[b][2][w], sel)};
-      const int d = 4 * dq + c;
-      const int off = d * Bf16Layout<D>::kRowBytesV + 16 * ((kq >> 1) ^ vt_swizzle(d)) + 8 * (kq & 1);
-      *reinterpret_cast<u32x2*>(smem + buf_off + off) = out;
-    }
-  }
-}
-
-__device__ __forceinline__ void wait_vm_and_barrier() {
-  // vmcnt(0): direct-to-LDS copies and register loads have landed.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-}
-
+// Scores of one tile, transposed: sacc[kb] = K[32kb + key_of_row(.)] Q^T.
 template <int D>
 __device__ __forceinline__ void score_tile(const char* smem, int kbuf, int arow, int hh,
                                            const bf16x8 (&qf)[D / 16], f32x16 (&sacc)[2]) {
   using Lay = Bf16Layout<D>;
+  bf16x8 a[2][D / 16];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    sacc[kb] = f32x16{};
     const int row = 32 * kb + arow;
-    const int rbase = kbuf + row * Lay::kRowBytesK;
+    const int rbase = kbuf + row * Lay::kRowBytes;
     const int sw = k_swizzle<D>(row);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a = lds_bf16x8(smem, rbase + 16 * ((2 * s + hh) ^ sw));
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+    for (int s = 0; s < D / 16; ++s) a[kb][s] = lds_bf16x8(smem, rbase + 16 * ((2 * s + hh) ^ sw));
+  }
+  sacc[0] = f32x16{};
+  sacc[1] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][s], qf[s], sacc[kb], 0, 0, 0);
+}
+
+// O^T[db] += V^T[32db.., 16-key step] P^T for the four 16-key steps of a tile.
+// Lane j of 16-lane group g points at 4 consecutive d of V row
+// key0 + j/4, where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2)
+// [+ 4 for the second read]; the transpose hands lane i the column d0 + i.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* smem, int vbuf, int lane,
+                                        const bf16x8 (&pf)[kBN / 16], f32x16 (&oacc)[D / 32]) {
+  using Lay = Bf16Layout<D>;
+  constexpr int kSteps = kBN / 16;              // 16-key steps per tile
+  constexpr int kMfmas = kSteps * (D / 32);     // MFMA i: step i / (D/32), block i % (D/32)
+  constexpr int kAhead = 2;                     // MFMAs whose operands are in flight
+  const int g = lane >> 4, j = lane & 15;
+  const int rsub = 8 * (g >> 1) + (j >> 2);     // row within a 16-key step (first read)
+  const int dsub = 16 * (g & 1) + 4 * (j & 3);  // d offset within a 32-d block
+  const uint32_t base = lds_address(smem) + vbuf;
+  auto issue = [&](int i, u32x2 (&v)[2]) {
+    const int s = i / (D / 32), db = i % (D / 32);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int row = 16 * s + rsub + 4 * h2;
+      const int d = 32 * db + dsub;
+      const int ch = (d >> 3) ^ v_swizzle<D>(row);
+      v[h2] = lds_tr16(base + row * Lay::kRowBytes + 16 * ch + 2 * (d & 7));
     }
+  };
+  u32x2 v[kAhead + 1][2];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) issue(i, v[i]);
+#pragma unroll
+  for (int i = 0; i < kMfmas; ++i) {
+    const int s = i / (D / 32), db = i % (D / 32);
+    u32x2 (&cur)[2] = v[i % (kAhead + 1)];
+    if (i + kAhead < kMfmas) {
+      issue(i + kAhead, v[(i + kAhead) % (kAhead + 1)]);
+      lds_wait<2 * kAhead>();
+    } else if (i + kAhead == kMfmas) {
+      lds_wait<2 * (kAhead - 1)>();
+    } else {
+      lds_wait<0>();
+    }
+    pin(cur[0]);
+    pin(cur[1]);
+    const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[s],
+                                                       oacc[db], 0, 0, 0);
+  }
+}
+
+// Row statistics combined across the two half-waves (lanes l and l ^ 32 hold
+// the two halves of a query column's keys).
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup -> (batch*head, query tile).  MI355X deals consecutive workgroup
+// ids round-robin over its 8 XCDs, each with its own L2.  Every XCD gets
+// whole heads, so the query tiles of a head share one L2 for their repeated
+// reads of that head's K and V.  Causal tiles differ in work (tile i streams
+// i+1 blocks of keys): within an XCD the ids then run longest tile first over
+// all of the XCD's heads, the longest-processing-time-first order that keeps
+// the XCD's CUs evenly loaded to the end.
+template <bool CAUSAL>
+__device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& qt) {
+  constexpr int kXcds = 8;
+  if (BH % kXcds == 0) {
+    const int hp = BH / kXcds;            // heads per XCD
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    if (CAUSAL) {
+      qt = nq - 1 - slot / hp;
+      bh = xcd * hp + slot % hp;
+    } else {
+      bh = xcd * hp + slot / nq;
+      qt = slot % nq;
+    }
+  } else if (CAUSAL) {
+    qt = nq - 1 - bid / BH;
+    bh = bid % BH;
+  } else {
+    bh = bid / nq;
+    qt = bid % nq;
   }
 }
 
@@ -183,9 +276,10 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Lse, int N,
-    int num_qtiles, int total_blocks, float scale, float scale_log2) {
+    int BH, int num_qtiles, float scale, float scale_log2) {
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
+  constexpr int kVmPerIter = 2 * Lay::kLoadsPerWave;  // direct loads a wave issues per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -193,10 +287,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   const int qi = lane & 31;  // query column of this lane inside the wave's 32
   const int hh = lane >> 5;  // half-wave
 
-  const int logical = xcd_remap(blockIdx.x, total_blocks);
-  const int bh = logical / num_qtiles;
-  int qt = logical - bh * num_qtiles;
-  if (CAUSAL) qt = num_qtiles - 1 - qt;  // longest rows first
+  int bh, qt;
+  map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
   const int q0 = qt * kBM;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qb = Q + head;
@@ -214,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     const int wave_end = CAUSAL ? min(N, wq0 + 32) : N;
     my_tiles = (wave_end + kBN - 1) / kBN;
   }
+  const int last = n_tiles - 1;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds d = 16s + 8hh + (0..7).
   bf16x8 qf[D / 16];
@@ -237,33 +330,32 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   float l_run = 0.f;  // this half-wave's part of the denominator
   const int arow = key_of_row(qi);
 
-  // Prologue: K_0, K_1 and V_0 into LDS.
-  VStage<D> vst;
-  load_k_tile_direct<D>(smem, Lay::kOffK0, Kb, 0, N, wave, lane);
-  if (n_tiles > 1) load_k_tile_direct<D>(smem, Lay::kOffK1, Kb, kBN, N, wave, lane);
-  load_v_tile<D>(vst, Vb, 0, N, tid);
-  store_vt_tile<D>(smem, Lay::kOffV0, vst, tid);
-  wait_vm_and_barrier();
+  auto kbuf = [](int t) { return Lay::kOffK + (t % kStages) * Lay::kTileBytes; };
+  auto vbuf = [](int t) { return Lay::kOffV + (t % kStages) * Lay::kTileBytes; };
+
+  // Prologue: K_0, K_1, V_0, V_1, K_2 in flight; wait for the first three.
+  load_tile_direct<D, false>(smem, kbuf(0), Kb, 0, N, wave, lane);
+  load_tile_direct<D, false>(smem, kbuf(1), Kb, min(1, last) * kBN, N, wave, lane);
+  load_tile_direct<D, true>(smem, vbuf(0), Vb, 0, N, wave, lane);
+  load_tile_direct<D, true>(smem, vbuf(1), Vb, min(1, last) * kBN, N, wave, lane);
+  load_tile_direct<D, false>(smem, kbuf(2), Kb, min(2, last) * kBN, N, wave, lane);
+  wait_vmcnt<kVmPerIter>();
+  block_sync();
 
   f32x16 sacc[2];
-  if (my_tiles > 0) score_tile<D>(smem, Lay::kOffK0, arow, hh, qf, sacc);
+  if (my_tiles > 0) score_tile<D>(smem, kbuf(0), arow, hh, qf, sacc);
 
   for (int t = 0; t < n_tiles; ++t) {
     const int kv0 = t * kBN;
-    const int kcur = (t & 1) ? Lay::kOffK1 : Lay::kOffK0;   // holds K_t (consumed)
-    const int knext = (t & 1) ? Lay::kOffK0 : Lay::kOffK1;  // holds K_{t+1}
-    const int vcur = (t & 1) ? Lay::kOffV1 : Lay::kOffV0;   // holds V_t
-    const int vnext = (t & 1) ? Lay::kOffV0 : Lay::kOffV1;  // receives V_{t+1}
-
-    // Prefetch: V_{t+1} into registers, K_{t+2} straight into the buffer K_t left.
-    if (t + 1 < n_tiles) load_v_tile<D>(vst, Vb, kv0 + kBN, N, tid);
-    if (t + 2 < n_tiles) load_k_tile_direct<D>(smem, kcur, Kb, kv0 + 2 * kBN, N, wave, lane);
+    // Loads for later iterations: K_{t+3} into the buffer K_t left (read in the
+    // previous iteration), V_{t+2} into the buffer V_{t-1} left.  Tile indices
+    // past the end are clamped, so every iteration issues the same number of
+    // loads and the vmcnt below stays exact.
+    load_tile_direct<D, false>(smem, kbuf(t), Kb, min(t + 3, last) * kBN, N, wave, lane);
+    load_tile_direct<D, true>(smem, vbuf(t + 2), Vb, min(t + 2, last) * kBN, N, wave, lane);
 
     if (t < my_tiles) {
-      // Scores of the next tile first, so the MFMAs run under this tile's softmax.
-      f32x16 snext[2];
-      if (t + 1 < my_tiles) score_tile<D>(smem, knext, arow, hh, qf, snext);
-
+      // Mask keys past N and, for causal, keys after the row (diagonal tiles only).
       // sacc element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
       const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
       if (need_mask) {
@@ -276,34 +368,40 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
           }
       }
 
-      float mx = kNegInf;
+      // Stream 1: scores of tile t+1 (MFMA).  Stream 2: softmax of tile t (VALU).
+      f32x16 snext[2];
+      score_tile<D>(smem, kbuf(t + 1), arow, hh, qf, snext);
+
+      float m8[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
-      mx = fmaxf(mx, other_half(mx));
+      for (int i = 0; i < 8; ++i) {
+        const int kb = i >> 2, e = 4 * (i & 3);
+        m8[i] = fmaxf(fmaxf(sacc[kb][e], sacc[kb][e + 1]), fmaxf(sacc[kb][e + 2], sacc[kb][e + 3]));
+      }
+      float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      mx = max_halves(mx);
       const float cand = mx * scale_log2;  // -inf for a fully masked tile
       const bool need = cand > base_run + kTau;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float base_new = need ? cand : base_run;
-        const float alpha = fast_exp2(base_run - base_new);
-        if (need) m_ref = mx;
-        base_run = base_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      }
+      const float base_new = need ? cand : base_run;
+      const float alpha = fast_exp2(base_run - base_new);
+      m_ref = need ? mx : m_ref;
+      base_run = base_new;
 
-      float lsum = 0.f;
+      float ps[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 8; ++i) {
+        const int kb = i >> 2, e = 4 * (i & 3);
+        float p[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, -base_run));
-          sacc[kb][e] = p;
-          lsum += p;
+        for (int u = 0; u < 4; ++u) {
+          p[u] = fast_exp2(__builtin_fmaf(sacc[kb][e + u], scale_log2, -base_run));
+          sacc[kb][e + u] = p[u];
         }
-      l_run += lsum;
+        ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      const float lsum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+      l_run = __builtin_fmaf(l_run, alpha, lsum);
 
       // P^T as the B operand of O^T += V^T P^T: 16-key step s2 takes elements
       // 8(s2%2) .. 8(s2%2)+7 of score block s2/2, i.e. keys 16 s2 + 8hh + (0..7).
@@ -313,27 +411,44 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[s2][j] = (__bf16)sacc[s2 >> 1][8 * (s2 & 1) + j];
 
+      // Keep the softmax ahead of the rescale branch (the compiler would sink it
+      // past the branch, next to its only use), so that it shares this block
+      // with the score MFMAs.
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + qi;
-        const int rbase = vcur + d * Lay::kRowBytesV;
-        const int sw = vt_swizzle(d);
-#pragma unroll
-        for (int s2 = 0; s2 < kBN / 16; ++s2) {
-          const bf16x8 a = lds_bf16x8(smem, rbase + 16 * ((2 * s2 + hh) ^ sw));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], oacc[db], 0, 0, 0);
-        }
+      for (int s2 = 0; s2 < kBN / 16; ++s2) {
+        u32x4 w = __builtin_bit_cast(u32x4, pf[s2]);
+        asm volatile("" : "+v"(w));
+        pf[s2] = __builtin_bit_cast(bf16x8, w);
       }
+      asm volatile("" : "+v"(l_run));
+
+      // Interleave: 4 operand reads ahead, then MFMA / VALU / read.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      }
+
+      pv_tile<D>(smem, vbuf(t), lane, pf, oacc);
       sacc[0] = snext[0];
       sacc[1] = snext[1];
     }
 
-    if (t + 1 < n_tiles) store_vt_tile<D>(smem, vnext, vst, tid);
-    wait_vm_and_barrier();
+    // K_{t+2} and V_{t+1} (issued last iteration) must have landed for every
+    // wave before anyone reads them; this iteration's loads may stay in flight.
+    wait_vmcnt<kVmPerIter>();
+    block_sync();
   }
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* orow = O + head + (size_t)qrow * D;
