@@ -22,12 +22,15 @@
 //    A-operand rows of the score MFMA are mapped to keys by `key_of_row` so
 //    that each half-wave holds 8 consecutive keys per 16-key step.
 //  * K and V tiles go from global memory straight into LDS
-//    (global_load_lds_dwordx4, no registers), row-major with XOR-swizzled
-//    16-byte chunks, in a ring of three buffers each: K is fetched three tiles
-//    ahead of its use and V two, so a load has two loop iterations to land.
-//    K rows are read as MFMA A operands with ds_read_b128; V^T operands come
-//    from the row-major V tile through ds_read_b64_tr_b16, whose 16-lane
-//    transpose turns four 8-byte row pieces into one column fragment.
+//    (global_load_lds_dwordx4, no registers) in a ring of three buffers each:
+//    K is fetched three tiles ahead of its use and V two, so a load has two
+//    loop iterations to land.  The LDS layouts are cut so that every operand
+//    read of a lane is one base register plus a compile-time offset and no
+//    read has bank conflicts: K is stored in 32-byte column slabs (one per
+//    16-wide step of d), V in 64-byte column slabs (one per 32-wide block of
+//    d).  K rows are read as MFMA A operands with ds_read_b128; V^T operands
+//    come from the V slabs through ds_read_b64_tr_b16, whose 16-lane transpose
+//    turns four 8-byte row pieces into one column fragment.
 //  * Per iteration a wave runs two interleaved streams: the score MFMAs of
 //    tile j+1 under the softmax VALU work of tile j, then the P V MFMAs of
 //    tile j under the issue of the next loads.  One barrier per tile.
@@ -40,6 +43,8 @@
 //    v_exp_f32 (base 2); L is formed in natural-log units at the end.
 #pragma once
 
+#include <utility>
+
 #include "fa_common.hpp"
 
 namespace fa355 {
@@ -51,10 +56,15 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 3;     // ring depth of the K and V tile buffers
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
 
+// LDS image of one tile (64 keys x D, bf16):
+//   K: D/16 slabs of [64 rows][32 bytes] (d = 16s .. 16s+15 of every key), the
+//      two 16-byte halves of row r swapped when bit 3 of r is set;
+//   V: D/32 slabs of [64 rows][64 bytes] (d = 32db .. 32db+31 of every key).
 template <int D>
 struct Bf16Layout {
   static constexpr int kTileBytes = kBN * D * 2;      // one K or V tile
-  static constexpr int kRowBytes = 2 * D;             // one K or V row
+  static constexpr int kKSlab = kBN * 32;             // 2 KB
+  static constexpr int kVSlab = kBN * 64;             // 4 KB
   static constexpr int kOffK = 0;                     // kStages K tiles
   static constexpr int kOffV = kStages * kTileBytes;  // kStages V tiles
   static constexpr int kBytes = 2 * kStages * kTileBytes;  // 96 KB at d = 128
@@ -62,20 +72,6 @@ struct Bf16Layout {
   static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
   static_assert(kLoadsPerWave >= 1 && kLoadsPerTile % kWaves == 0, "tile split over waves");
 };
-
-// 16-byte chunk swizzles (chunk index XOR a function of the row).  K: keeps the
-// ds_read_b128 operand reads (32 rows x 2 chunks per instruction) conflict
-// free.  V: the transpose reads of one instruction touch 8 rows {r0..r0+3,
-// r0+8..r0+11} x 4 chunks; XOR-ing the chunk's upper bits with the row spreads
-// them evenly over the banks.
-template <int D>
-__device__ __forceinline__ int k_swizzle(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swizzle(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
 
 // Key (within a 32-key block) fed to A-operand row i of the score MFMA.  With
 // i = 8g + 4h + r (g = 0..3, h = 0..1, r = 0..3) the accumulator element
@@ -86,8 +82,20 @@ __device__ __forceinline__ int key_of_row(int i) {
   return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + r;
 }
 
-__device__ __forceinline__ bf16x8 lds_bf16x8(const char* smem, int byte_off) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + byte_off));
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, with i usable as a constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ uint32_t lds_address(const char* p) {
+  // generic -> LDS address-space cast; the LDS pointer's value is the offset
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
@@ -95,9 +103,20 @@ __device__ __forceinline__ bf16x8 lds_bf16x8(const char* smem, int byte_off) {
 // at, e = 0..3.  Issued from inline asm: the compiler would otherwise wait for
 // every outstanding direct-to-LDS load before it, which defeats the prefetch.
 // The caller waits for the result with lds_wait<N>() and pins it with pin().
+template <int OFF>
 __device__ __forceinline__ u32x2 lds_tr16(uint32_t lds_addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   u32x2 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "n"(OFF));
+  return v;
+}
+// Plain 16-byte LDS read, issued from inline asm so that its place among the
+// other operand reads is fixed (see lds_tr16).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read128(uint32_t lds_addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "n"(OFF));
   return v;
 }
 template <int N>
@@ -107,47 +126,16 @@ __device__ __forceinline__ void lds_wait() {
 // Orders every later use of v after the preceding lds_wait (asm statements
 // keep their relative order; the use depends on this one's output).
 __device__ __forceinline__ void pin(u32x2& v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ uint32_t lds_address(const char* p) {
-  // generic -> LDS address-space cast; the LDS pointer's value is the offset
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
-}
+__device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Workgroup barrier without the memory fence of __syncthreads(), whose
 // implied vmcnt(0) would also wait for the loads that are meant to stay in
-// flight across it.  The callers wait for exactly the loads they need first.
+// flight across it.  The callers wait for exactly the loads they need first,
+// and every LDS read before it has been consumed (waited for) already.
 __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// Direct global->LDS copy of one K or V tile (swizzled rows).  Each wave
-// issues kLoadsPerWave instructions; lane i of an instruction fills physical
-// bytes [16i, 16i+16) of its 1 KB slice, so it fetches the logical chunk that
-// the swizzle puts there.  Rows past N are clamped to row N-1: their scores
-// are masked and their probabilities are 0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
-                                                 const uint16_t* __restrict__ src_head, int kv0,
-                                                 int N, int wave, int lane) {
-  using Lay = Bf16Layout<D>;
-#pragma unroll
-  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
-    const int slice = wave * Lay::kLoadsPerWave + r;
-    const int phys = slice * 1024 + 16 * lane;
-    const int row = phys / Lay::kRowBytes;
-    const int pch = (phys % Lay::kRowBytes) / 16;
-    const int ch = pch ^ (IS_V ? v_swizzle<D>(row) : k_swizzle<D>(row));
-    const int key = min(kv0 + row, N - 1);
-    const uint16_t* src = src_head + (size_t)key * D + 8 * ch;
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<__attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(src)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(
-            reinterpret_cast<uintptr_t>(smem + buf_off + slice * 1024)),
-        16, 0, 0);
-  }
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their
@@ -158,75 +146,112 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Scores of one tile, transposed: sacc[kb] = K[32kb + key_of_row(.)] Q^T.
-template <int D>
-__device__ __forceinline__ void score_tile(const char* smem, int kbuf, int arow, int hh,
-                                           const bf16x8 (&qf)[D / 16], f32x16 (&sacc)[2]) {
+// Direct global->LDS copy of one K or V tile.  Each wave issues kLoadsPerWave
+// instructions; lane l of instruction (slice) i fills bytes [16l, 16l+16) of
+// the tile's i-th kilobyte and fetches the 16 bytes of K or V that the layout
+// puts there.  Rows past N are clamped to row N-1: their scores are masked and
+// their probabilities are 0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
+                                                 const uint16_t* __restrict__ src_head, int kv0,
+                                                 int N, int wave, int lane) {
   using Lay = Bf16Layout<D>;
-  bf16x8 a[2][D / 16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = 32 * kb + arow;
-    const int rbase = kbuf + row * Lay::kRowBytes;
-    const int sw = k_swizzle<D>(row);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) a[kb][s] = lds_bf16x8(smem, rbase + 16 * ((2 * s + hh) ^ sw));
+  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
+    const int slice = wave * Lay::kLoadsPerWave + r;
+    int row, col;
+    if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
+      row = 16 * (slice & 3) + (lane >> 2);
+      col = 32 * (slice >> 2) + 8 * (lane & 3);
+    } else {     // slab s = slice / 2 holds rows 32 (slice % 2) .. +31
+      row = 32 * (slice & 1) + (lane >> 1);
+      col = 16 * (slice >> 1) + 8 * ((lane & 1) ^ ((row >> 3) & 1));
+    }
+    const int key = min(kv0 + row, N - 1);
+    const uint16_t* src = src_head + (size_t)key * D + col;
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<__attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(src)),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(
+            reinterpret_cast<uintptr_t>(smem + buf_off + slice * 1024)),
+        16, 0, 0);
   }
+}
+
+// Scores of one tile, transposed: sacc[kb] = K[32kb + key_of_row(.)] Q^T.
+// kaddr = LDS address of this lane's K piece in slab 0, block 0: row
+// key_of_row(qi), half hh (swapped by the row's bit 3); slab s and block kb add
+// constants.  The operand reads run kAhead MFMAs ahead of their use, in a
+// rotation of kAhead + 2 register slots (a slot is refilled two MFMAs after
+// the one that read it).
+template <int D>
+__device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D / 16],
+                                           f32x16 (&sacc)[2]) {
+  using Lay = Bf16Layout<D>;
+  constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
+  constexpr int kAhead = 3;
+  constexpr int kSlots = kAhead + 2;
+  u32x4 a[kSlots];
+  auto issue = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    a[i % kSlots] = lds_read128<(i / 2) * Lay::kKSlab + (i % 2) * 1024>(kaddr);
+  };
+  static_for<kAhead>(issue);
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][s], qf[s], sacc[kb], 0, 0, 0);
+  static_for<kMfmas>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + kAhead < kMfmas) {
+      issue(std::integral_constant<int, i + kAhead>{});
+      lds_wait<kAhead>();
+    } else {
+      lds_wait<kMfmas - 1 - i>();
+    }
+    pin(a[i % kSlots]);
+    sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i % kSlots]),
+                                                         qf[i / 2], sacc[i % 2], 0, 0, 0);
+  });
 }
 
 // O^T[db] += V^T[32db.., 16-key step] P^T for the four 16-key steps of a tile.
-// Lane j of 16-lane group g points at 4 consecutive d of V row
-// key0 + j/4, where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2)
-// [+ 4 for the second read]; the transpose hands lane i the column d0 + i.
+// Lane j of 16-lane group g points at 4 consecutive d of V row key0 + j/4,
+// where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2) [+ 4 for the
+// second read]; the transpose hands lane i the column d0 + i.  vaddr = LDS
+// address of this lane's piece in slab 0, step 0, first read.
 template <int D>
-__device__ __forceinline__ void pv_tile(const char* smem, int vbuf, int lane,
-                                        const bf16x8 (&pf)[kBN / 16], f32x16 (&oacc)[D / 32]) {
+__device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN / 16],
+                                        f32x16 (&oacc)[D / 32]) {
   using Lay = Bf16Layout<D>;
-  constexpr int kSteps = kBN / 16;              // 16-key steps per tile
-  constexpr int kMfmas = kSteps * (D / 32);     // MFMA i: step i / (D/32), block i % (D/32)
+  constexpr int kBlocks = D / 32;
+  constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
   constexpr int kAhead = 2;                     // MFMAs whose operands are in flight
-  const int g = lane >> 4, j = lane & 15;
-  const int rsub = 8 * (g >> 1) + (j >> 2);     // row within a 16-key step (first read)
-  const int dsub = 16 * (g & 1) + 4 * (j & 3);  // d offset within a 32-d block
-  const uint32_t base = lds_address(smem) + vbuf;
-  auto issue = [&](int i, u32x2 (&v)[2]) {
-    const int s = i / (D / 32), db = i % (D / 32);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int row = 16 * s + rsub + 4 * h2;
-      const int d = 32 * db + dsub;
-      const int ch = (d >> 3) ^ v_swizzle<D>(row);
-      v[h2] = lds_tr16(base + row * Lay::kRowBytes + 16 * ch + 2 * (d & 7));
-    }
+  constexpr int kSlots = kAhead + 2;            // a slot is refilled two MFMAs after its use
+  u32x2 v[kSlots][2];
+  auto issue = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int s = i / kBlocks, db = i % kBlocks;
+    constexpr int off = db * Lay::kVSlab + s * 16 * 64;
+    v[i % kSlots][0] = lds_tr16<off>(vaddr);
+    v[i % kSlots][1] = lds_tr16<off + 4 * 64>(vaddr);
   };
-  u32x2 v[kAhead + 1][2];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) issue(i, v[i]);
-#pragma unroll
-  for (int i = 0; i < kMfmas; ++i) {
-    const int s = i / (D / 32), db = i % (D / 32);
-    u32x2 (&cur)[2] = v[i % (kAhead + 1)];
-    if (i + kAhead < kMfmas) {
-      issue(i + kAhead, v[(i + kAhead) % (kAhead + 1)]);
+  static_for<kAhead>(issue);
+  static_for<kMfmas>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int s = i / kBlocks, db = i % kBlocks;
+    if constexpr (i + kAhead < kMfmas) {
+      issue(std::integral_constant<int, i + kAhead>{});
       lds_wait<2 * kAhead>();
-    } else if (i + kAhead == kMfmas) {
+    } else if constexpr (i + kAhead == kMfmas) {
       lds_wait<2 * (kAhead - 1)>();
     } else {
       lds_wait<0>();
     }
+    u32x2(&cur)[2] = v[i % kSlots];
     pin(cur[0]);
     pin(cur[1]);
     const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[s],
                                                        oacc[db], 0, 0, 0);
-  }
+  });
 }
 
 // Row statistics combined across the two half-waves (lanes l and l ^ 32 hold
@@ -328,35 +353,49 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   float base_run = -__FLT_MAX__;
   float m_ref = kNegInf;
   float l_run = 0.f;  // this half-wave's part of the denominator
-  const int arow = key_of_row(qi);
 
-  auto kbuf = [](int t) { return Lay::kOffK + (t % kStages) * Lay::kTileBytes; };
-  auto vbuf = [](int t) { return Lay::kOffV + (t % kStages) * Lay::kTileBytes; };
+  // Per-lane operand offsets (constant over the loop).
+  const int arow = key_of_row(qi);
+  const int k_lane = arow * 32 + 16 * (hh ^ ((arow >> 3) & 1));
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_lane = (8 * (g16 >> 1) + (j16 >> 2)) * 64 + 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+  const uint32_t smem_lds = lds_address(smem);
 
   // Prologue: K_0, K_1, V_0, V_1, K_2 in flight; wait for the first three.
-  load_tile_direct<D, false>(smem, kbuf(0), Kb, 0, N, wave, lane);
-  load_tile_direct<D, false>(smem, kbuf(1), Kb, min(1, last) * kBN, N, wave, lane);
-  load_tile_direct<D, true>(smem, vbuf(0), Vb, 0, N, wave, lane);
-  load_tile_direct<D, true>(smem, vbuf(1), Vb, min(1, last) * kBN, N, wave, lane);
-  load_tile_direct<D, false>(smem, kbuf(2), Kb, min(2, last) * kBN, N, wave, lane);
+  // Ring slots: tile t lives in slot t % 3 of its ring.
+  load_tile_direct<D, false>(smem, Lay::kOffK, Kb, 0, N, wave, lane);
+  load_tile_direct<D, false>(smem, Lay::kOffK + Lay::kTileBytes, Kb, min(1, last) * kBN, N, wave,
+                             lane);
+  load_tile_direct<D, true>(smem, Lay::kOffV, Vb, 0, N, wave, lane);
+  load_tile_direct<D, true>(smem, Lay::kOffV + Lay::kTileBytes, Vb, min(1, last) * kBN, N, wave,
+                            lane);
+  load_tile_direct<D, false>(smem, Lay::kOffK + 2 * Lay::kTileBytes, Kb, min(2, last) * kBN, N,
+                             wave, lane);
   wait_vmcnt<kVmPerIter>();
   block_sync();
 
-  f32x16 sacc[2];
-  if (my_tiles > 0) score_tile<D>(smem, kbuf(0), arow, hh, qf, sacc);
+  f32x16 sA[2], sB[2];
+  if (my_tiles > 0) score_tile<D>(smem_lds + Lay::kOffK + k_lane, qf, sA);
+  // Every wave is done reading K_0 before its slot is refilled below.
+  block_sync();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // One tile.  Slots: a = t % 3 (K_t, V_t), b = (t+1) % 3 (K_{t+1}),
+  // c = (t+2) % 3 (V_{t+2}); cur holds the raw scores of tile t, nxt receives
+  // those of tile t+1.
+  auto iteration = [&](int t, int a, int b, int c, f32x16(&cur)[2], f32x16(&nxt)[2]) {
     const int kv0 = t * kBN;
-    // Loads for later iterations: K_{t+3} into the buffer K_t left (read in the
-    // previous iteration), V_{t+2} into the buffer V_{t-1} left.  Tile indices
+    // Loads for later iterations: K_{t+3} into the slot K_t left (read in the
+    // previous iteration), V_{t+2} into the slot V_{t-1} left.  Tile indices
     // past the end are clamped, so every iteration issues the same number of
     // loads and the vmcnt below stays exact.
-    load_tile_direct<D, false>(smem, kbuf(t), Kb, min(t + 3, last) * kBN, N, wave, lane);
-    load_tile_direct<D, true>(smem, vbuf(t + 2), Vb, min(t + 2, last) * kBN, N, wave, lane);
+    load_tile_direct<D, false>(smem, Lay::kOffK + a * Lay::kTileBytes, Kb,
+                               min(t + 3, last) * kBN, N, wave, lane);
+    load_tile_direct<D, true>(smem, Lay::kOffV + c * Lay::kTileBytes, Vb, min(t + 2, last) * kBN,
+                              N, wave, lane);
 
     if (t < my_tiles) {
       // Mask keys past N and, for causal, keys after the row (diagonal tiles only).
-      // sacc element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
+      // cur element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
       const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
       if (need_mask) {
 #pragma unroll
@@ -364,19 +403,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
-            if (key >= N || (CAUSAL && key > qrow)) sacc[kb][e] = kNegInf;
+            if (key >= N || (CAUSAL && key > qrow)) cur[kb][e] = kNegInf;
           }
       }
 
       // Stream 1: scores of tile t+1 (MFMA).  Stream 2: softmax of tile t (VALU).
-      f32x16 snext[2];
-      score_tile<D>(smem, kbuf(t + 1), arow, hh, qf, snext);
+      score_tile<D>(smem_lds + Lay::kOffK + b * Lay::kTileBytes + k_lane, qf, nxt);
 
       float m8[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kb = i >> 2, e = 4 * (i & 3);
-        m8[i] = fmaxf(fmaxf(sacc[kb][e], sacc[kb][e + 1]), fmaxf(sacc[kb][e + 2], sacc[kb][e + 3]));
+        m8[i] = fmaxf(fmaxf(cur[kb][e], cur[kb][e + 1]), fmaxf(cur[kb][e + 2], cur[kb][e + 3]));
       }
       float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
                        fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
@@ -395,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = fast_exp2(__builtin_fmaf(sacc[kb][e + u], scale_log2, -base_run));
-          sacc[kb][e + u] = p[u];
+          p[u] = fast_exp2(__builtin_fmaf(cur[kb][e + u], scale_log2, -base_run));
+          cur[kb][e + u] = p[u];
         }
         ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
       }
@@ -409,7 +447,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < kBN / 16; ++s2)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[s2][j] = (__bf16)sacc[s2 >> 1][8 * (s2 & 1) + j];
+        for (int j = 0; j < 8; ++j) pf[s2][j] = (__bf16)cur[s2 >> 1][8 * (s2 & 1) + j];
+
+      // Interleave: ~10 VALU ops of the softmax under each score MFMA.
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);
+      }
 
       // Keep the softmax ahead of the rescale branch (the compiler would sink it
       // past the branch, next to its only use), so that it shares this block
@@ -422,30 +467,32 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
       }
       asm volatile("" : "+v"(l_run));
 
-      // Interleave: 4 operand reads ahead, then MFMA / VALU / read.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
       }
 
-      pv_tile<D>(smem, vbuf(t), lane, pf, oacc);
-      sacc[0] = snext[0];
-      sacc[1] = snext[1];
+      pv_tile<D>(smem_lds + Lay::kOffV + a * Lay::kTileBytes + v_lane, pf, oacc);
     }
 
     // K_{t+2} and V_{t+1} (issued last iteration) must have landed for every
     // wave before anyone reads them; this iteration's loads may stay in flight.
     wait_vmcnt<kVmPerIter>();
     block_sync();
+  };
+
+  // Two tiles per trip so that the two score buffers swap roles instead of
+  // being copied.
+  int t = 0, a = 0, b = 1, c = 2;
+  for (; t + 1 < n_tiles; t += 2) {
+    iteration(t, a, b, c, sA, sB);
+    iteration(t + 1, b, c, a, sB, sA);
+    const int a2 = c, b2 = a, c2 = b;  // slots advance by two
+    a = a2;
+    b = b2;
+    c = c2;
   }
+  if (t < n_tiles) iteration(t, a, b, c, sA, sB);
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
   const float l_tot = sum_halves(l_run);
