@@ -22,18 +22,21 @@
 //    A-operand rows of the score MFMA are mapped to keys by `key_of_row` so
 //    that each half-wave holds 8 consecutive keys per 16-key step.
 //  * K and V tiles go from global memory straight into LDS
-//    (global_load_lds_dwordx4, no registers) in a ring of three buffers each:
-//    K is fetched three tiles ahead of its use and V two, so a load has two
-//    loop iterations to land.  The LDS layouts are cut so that every operand
+//    (global_load_lds_dwordx4, no registers) in a ring of three buffers each,
+//    each tile issued two loop iterations before the one that reads it.  The LDS layouts are cut so that every operand
 //    read of a lane is one base register plus a compile-time offset and no
 //    read has bank conflicts: K is stored in 32-byte column slabs (one per
 //    16-wide step of d), V in 64-byte column slabs (one per 32-wide block of
 //    d).  K rows are read as MFMA A operands with ds_read_b128; V^T operands
 //    come from the V slabs through ds_read_b64_tr_b16, whose 16-lane transpose
 //    turns four 8-byte row pieces into one column fragment.
-//  * Per iteration a wave runs two interleaved streams: the score MFMAs of
-//    tile j+1 under the softmax VALU work of tile j, then the P V MFMAs of
-//    tile j under the issue of the next loads.  One barrier per tile.
+//  * The softmax VALU work of a tile is split over both MFMA streams of the
+//    loop so that every MFMA has VALU work to hide: iteration j runs the
+//    P V MFMAs of tile j under the mask, row maximum, reference update and
+//    first half of the exponentials of tile j+1, then the score MFMAs of tile
+//    j+2 under the second half of those exponentials, the row sums and the
+//    bf16 conversion.  sched_group_barrier interleaves each pair; the operand
+//    reads are issued a few MFMAs ahead from inline asm.  One barrier per tile.
 //  * The reference point of the online softmax moves only when a row's maximum
 //    grows by more than 2^8 (in base-2 units); until then probabilities are
 //    taken against the stale reference and are at most 2^8, which fp32 and
@@ -183,12 +186,11 @@ __device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
 // constants.  The operand reads run kAhead MFMAs ahead of their use, in a
 // rotation of kAhead + 2 register slots (a slot is refilled two MFMAs after
 // the one that read it).
-template <int D>
+template <int D, int kAhead = 6>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D / 16],
                                            f32x16 (&sacc)[2]) {
   using Lay = Bf16Layout<D>;
   constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
-  constexpr int kAhead = 3;
   constexpr int kSlots = kAhead + 2;
   u32x4 a[kSlots];
   auto issue = [&](auto ic) {
@@ -217,13 +219,12 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D 
 // where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2) [+ 4 for the
 // second read]; the transpose hands lane i the column d0 + i.  vaddr = LDS
 // address of this lane's piece in slab 0, step 0, first read.
-template <int D>
+template <int D, int kAhead = 4>
 __device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN / 16],
                                         f32x16 (&oacc)[D / 32]) {
   using Lay = Bf16Layout<D>;
   constexpr int kBlocks = D / 32;
   constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
-  constexpr int kAhead = 2;                     // MFMAs whose operands are in flight
   constexpr int kSlots = kAhead + 2;            // a slot is refilled two MFMAs after its use
   u32x2 v[kSlots][2];
   auto issue = [&](auto ic) {
@@ -240,10 +241,8 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN /
     if constexpr (i + kAhead < kMfmas) {
       issue(std::integral_constant<int, i + kAhead>{});
       lds_wait<2 * kAhead>();
-    } else if constexpr (i + kAhead == kMfmas) {
-      lds_wait<2 * (kAhead - 1)>();
     } else {
-      lds_wait<0>();
+      lds_wait<2 * (kMfmas - 1 - i)>();
     }
     u32x2(&cur)[2] = v[i % kSlots];
     pin(cur[0]);
@@ -304,7 +303,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     int BH, int num_qtiles, float scale, float scale_log2) {
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
-  constexpr int kVmPerIter = 2 * Lay::kLoadsPerWave;  // direct loads a wave issues per tile
+  constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
+  constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -360,124 +360,180 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   const int g16 = lane >> 4, j16 = lane & 15;
   const int v_lane = (8 * (g16 >> 1) + (j16 >> 2)) * 64 + 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
   const uint32_t smem_lds = lds_address(smem);
-
-  // Prologue: K_0, K_1, V_0, V_1, K_2 in flight; wait for the first three.
-  // Ring slots: tile t lives in slot t % 3 of its ring.
-  load_tile_direct<D, false>(smem, Lay::kOffK, Kb, 0, N, wave, lane);
-  load_tile_direct<D, false>(smem, Lay::kOffK + Lay::kTileBytes, Kb, min(1, last) * kBN, N, wave,
-                             lane);
-  load_tile_direct<D, true>(smem, Lay::kOffV, Vb, 0, N, wave, lane);
-  load_tile_direct<D, true>(smem, Lay::kOffV + Lay::kTileBytes, Vb, min(1, last) * kBN, N, wave,
-                            lane);
-  load_tile_direct<D, false>(smem, Lay::kOffK + 2 * Lay::kTileBytes, Kb, min(2, last) * kBN, N,
-                             wave, lane);
-  wait_vmcnt<kVmPerIter>();
-  block_sync();
-
-  f32x16 sA[2], sB[2];
-  if (my_tiles > 0) score_tile<D>(smem_lds + Lay::kOffK + k_lane, qf, sA);
-  // Every wave is done reading K_0 before its slot is refilled below.
-  block_sync();
-
-  // One tile.  Slots: a = t % 3 (K_t, V_t), b = (t+1) % 3 (K_{t+1}),
-  // c = (t+2) % 3 (V_{t+2}); cur holds the raw scores of tile t, nxt receives
-  // those of tile t+1.
-  auto iteration = [&](int t, int a, int b, int c, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-    const int kv0 = t * kBN;
-    // Loads for later iterations: K_{t+3} into the slot K_t left (read in the
-    // previous iteration), V_{t+2} into the slot V_{t-1} left.  Tile indices
-    // past the end are clamped, so every iteration issues the same number of
-    // loads and the vmcnt below stays exact.
-    load_tile_direct<D, false>(smem, Lay::kOffK + a * Lay::kTileBytes, Kb,
-                               min(t + 3, last) * kBN, N, wave, lane);
-    load_tile_direct<D, true>(smem, Lay::kOffV + c * Lay::kTileBytes, Vb, min(t + 2, last) * kBN,
+  auto k_addr = [&](int slot) { return smem_lds + Lay::kOffK + slot * Lay::kTileBytes + k_lane; };
+  auto v_addr = [&](int slot) { return smem_lds + Lay::kOffV + slot * Lay::kTileBytes + v_lane; };
+  auto load_k = [&](int slot, int tile) {
+    load_tile_direct<D, false>(smem, Lay::kOffK + slot * Lay::kTileBytes, Kb, min(tile, last) * kBN,
+                               N, wave, lane);
+  };
+  auto load_v = [&](int slot, int tile) {
+    load_tile_direct<D, true>(smem, Lay::kOffV + slot * Lay::kTileBytes, Vb, min(tile, last) * kBN,
                               N, wave, lane);
+  };
 
-    if (t < my_tiles) {
-      // Mask keys past N and, for causal, keys after the row (diagonal tiles only).
-      // cur element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
-      const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
-      if (need_mask) {
+  // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
+  // maximum, reference update, the exponentials of block 0 and their sum.
+  // Stage 2: the exponentials of block 1, the row sum into l_run, and P^T as
+  // bf16 B operands of O^T += V^T P^T (16-key step s2 takes elements
+  // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
+  // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
+  auto mask_tile = [&](int j, f32x16(&sc)[2]) {
+    const int kv0 = j * kBN;
+    const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
+    if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
-            if (key >= N || (CAUSAL && key > qrow)) cur[kb][e] = kNegInf;
-          }
-      }
-
-      // Stream 1: scores of tile t+1 (MFMA).  Stream 2: softmax of tile t (VALU).
-      score_tile<D>(smem_lds + Lay::kOffK + b * Lay::kTileBytes + k_lane, qf, nxt);
-
-      float m8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb = i >> 2, e = 4 * (i & 3);
-        m8[i] = fmaxf(fmaxf(cur[kb][e], cur[kb][e + 1]), fmaxf(cur[kb][e + 2], cur[kb][e + 3]));
-      }
-      float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-      mx = max_halves(mx);
-      const float cand = mx * scale_log2;  // -inf for a fully masked tile
-      const bool need = cand > base_run + kTau;
-      const float base_new = need ? cand : base_run;
-      const float alpha = fast_exp2(base_run - base_new);
-      m_ref = need ? mx : m_ref;
-      base_run = base_new;
-
-      float ps[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb = i >> 2, e = 4 * (i & 3);
-        float p[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          p[u] = fast_exp2(__builtin_fmaf(cur[kb][e + u], scale_log2, -base_run));
-          cur[kb][e + u] = p[u];
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
+          if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
         }
-        ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
+    }
+  };
+  auto stage1 = [&](f32x16(&sc)[2], float& alpha, bool& need, float& half_sum) {
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kb = i >> 2, e = 4 * (i & 3);
+      m8[i] = fmaxf(fmaxf(sc[kb][e], sc[kb][e + 1]), fmaxf(sc[kb][e + 2], sc[kb][e + 3]));
+    }
+    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                     fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    mx = max_halves(mx);
+    const float cand = mx * scale_log2;  // -inf for a fully masked tile
+    need = cand > base_run + kTau;
+    const float base_new = need ? cand : base_run;
+    alpha = fast_exp2(base_run - base_new);
+    m_ref = need ? mx : m_ref;
+    base_run = base_new;
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = fast_exp2(__builtin_fmaf(sc[0][4 * i + u], scale_log2, -base_run));
+        sc[0][4 * i + u] = p[u];
       }
-      const float lsum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-      l_run = __builtin_fmaf(l_run, alpha, lsum);
+      ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    half_sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  auto stage2 = [&](f32x16(&sc)[2], float alpha, float half_sum, bf16x8(&pfo)[kBN / 16]) {
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = fast_exp2(__builtin_fmaf(sc[1][4 * i + u], scale_log2, -base_run));
+        sc[1][4 * i + u] = p[u];
+      }
+      ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    const float lsum = half_sum + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    l_run = __builtin_fmaf(l_run, alpha, lsum);
+#pragma unroll
+    for (int s2 = 0; s2 < kBN / 16; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pfo[s2][j] = (__bf16)sc[s2 >> 1][8 * (s2 & 1) + j];
+  };
+  // Empty asm that ties values to this point of the program: the compiler
+  // would otherwise sink them past the next branch, next to their use.
+  auto pin_scores = [&](f32x16(&sc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 w = {__float_as_uint(sc[kb][4 * q]), __float_as_uint(sc[kb][4 * q + 1]),
+                   __float_as_uint(sc[kb][4 * q + 2]), __float_as_uint(sc[kb][4 * q + 3])};
+        pin(w);
+        sc[kb][4 * q] = __uint_as_float(w[0]);
+        sc[kb][4 * q + 1] = __uint_as_float(w[1]);
+        sc[kb][4 * q + 2] = __uint_as_float(w[2]);
+        sc[kb][4 * q + 3] = __uint_as_float(w[3]);
+      }
+  };
+  auto pin_probs = [&](bf16x8(&pfo)[kBN / 16]) {
+#pragma unroll
+    for (int s2 = 0; s2 < kBN / 16; ++s2) {
+      u32x4 w = __builtin_bit_cast(u32x4, pfo[s2]);
+      pin(w);
+      pfo[s2] = __builtin_bit_cast(bf16x8, w);
+    }
+    asm volatile("" : "+v"(l_run));
+  };
 
-      // P^T as the B operand of O^T += V^T P^T: 16-key step s2 takes elements
-      // 8(s2%2) .. 8(s2%2)+7 of score block s2/2, i.e. keys 16 s2 + 8hh + (0..7).
-      bf16x8 pf[kBN / 16];
-#pragma unroll
-      for (int s2 = 0; s2 < kBN / 16; ++s2)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf[s2][j] = (__bf16)cur[s2 >> 1][8 * (s2 & 1) + j];
+  // Prologue.  Ring slots: tile j lives in slot j % 3 of its ring.  Iteration
+  // t reads V_t and K_{t+2} and refills the slots of V_{t-1} and K_{t+1} with
+  // V_{t+2} and K_{t+4}; so before iteration 0, K_0..K_2 and V_0 must have
+  // landed and K_3, V_1 be in flight.
+  load_k(0, 0);
+  load_k(1, 1);
+  load_k(2, 2);
+  load_v(0, 0);
+  load_v(1, 1);
+  wait_vmcnt<kVmPerTile>();  // all but V_1
+  block_sync();
 
-      // Interleave: ~10 VALU ops of the softmax under each score MFMA.
+  f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
+  bf16x8 pf[kBN / 16];  // P^T of the tile whose P V is next
+  if (my_tiles > 0) {
+    score_tile<D>(k_addr(0), qf, sA);
+    score_tile<D>(k_addr(1), qf, sB);
+    mask_tile(0, sA);
+    float alpha, hs;
+    bool need;
+    stage1(sA, alpha, need, hs);
+    stage2(sA, alpha, hs, pf);
+  }
+  block_sync();  // every wave is done reading K_0 before its slot is refilled
+  load_k(0, 3);
+
+  // One tile.  Slots: a = t % 3, b = (t+1) % 3, c = (t+2) % 3.  On entry pf
+  // holds P_t and cur the raw scores of tile t+1; nxt receives tile t+2.
+  auto iteration = [&](int t, int a, int b, int c, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+    load_k(b, t + 4);
+    load_v(c, t + 2);
+
+    if (t + 1 < my_tiles) {
+      mask_tile(t + 1, cur);
+      // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU).
+      pv_tile<D>(v_addr(a), pf, oacc);
+      float alpha, hs;
+      bool need;
+      stage1(cur, alpha, need, hs);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
+      for (int i = 0; i < kMf; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
       }
+      pin_scores(cur);
+      asm volatile("" : "+v"(hs), "+v"(alpha));
 
-      // Keep the softmax ahead of the rescale branch (the compiler would sink it
-      // past the branch, next to its only use), so that it shares this block
-      // with the score MFMAs.
-#pragma unroll
-      for (int s2 = 0; s2 < kBN / 16; ++s2) {
-        u32x4 w = __builtin_bit_cast(u32x4, pf[s2]);
-        asm volatile("" : "+v"(w));
-        pf[s2] = __builtin_bit_cast(bf16x8, w);
-      }
-      asm volatile("" : "+v"(l_run));
-
+      // Phase 2: move the output to the new reference (rare).
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
       }
 
-      pv_tile<D>(smem_lds + Lay::kOffV + a * Lay::kTileBytes + v_lane, pf, oacc);
+      // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU).
+      score_tile<D>(k_addr(c), qf, nxt);
+      stage2(cur, alpha, hs, pf);
+#pragma unroll
+      for (int i = 0; i < kMf; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+      }
+      pin_probs(pf);
+    } else if (t < my_tiles) {
+      pv_tile<D>(v_addr(a), pf, oacc);
     }
 
-    // K_{t+2} and V_{t+1} (issued last iteration) must have landed for every
-    // wave before anyone reads them; this iteration's loads may stay in flight.
-    wait_vmcnt<kVmPerIter>();
+    // K_{t+3} and V_{t+1} (issued one iteration earlier) must have landed for
+    // every wave before anyone reads them; this iteration's loads may stay in
+    // flight.
+    wait_vmcnt<2 * kVmPerTile>();
     block_sync();
   };
 
@@ -485,14 +541,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   // being copied.
   int t = 0, a = 0, b = 1, c = 2;
   for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, a, b, c, sA, sB);
-    iteration(t + 1, b, c, a, sB, sA);
+    iteration(t, a, b, c, sB, sA);
+    iteration(t + 1, b, c, a, sA, sB);
     const int a2 = c, b2 = a, c2 = b;  // slots advance by two
     a = a2;
     b = b2;
     c = c2;
   }
-  if (t < n_tiles) iteration(t, a, b, c, sA, sB);
+  if (t < n_tiles) iteration(t, a, b, c, sB, sA);
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
   const float l_tot = sum_halves(l_run);
