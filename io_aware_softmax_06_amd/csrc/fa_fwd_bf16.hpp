@@ -56,7 +56,11 @@ constexpr int kBM = 256;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 3;     // ring depth of the K and V tile buffers
+#ifndef FA355_BF16_STAGES
+#define FA355_BF16_STAGES 3
+#endif
+constexpr int kStages = FA355_BF16_STAGES;  // ring depth of the K and V tile buffers
+static_assert(kStages >= 3, "the loop reads K two tiles ahead of V");
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
 
 // LDS image of one tile (64 keys x D, bf16):
@@ -70,7 +74,8 @@ struct Bf16Layout {
   static constexpr int kVSlab = kBN * 64;             // 4 KB
   static constexpr int kOffK = 0;                     // kStages K tiles
   static constexpr int kOffV = kStages * kTileBytes;  // kStages V tiles
-  static constexpr int kBytes = 2 * kStages * kTileBytes;  // 96 KB at d = 128
+  static constexpr int kBytes = 2 * kStages * kTileBytes;  // 32 KB per stage at d = 128
+  static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
   static constexpr int kLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
   static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
   static_assert(kLoadsPerWave >= 1 && kLoadsPerTile % kWaves == 0, "tile split over waves");
@@ -155,12 +160,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // puts there.  Rows past N are clamped to row N-1: their scores are masked and
 // their probabilities are 0.
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
-                                                 const uint16_t* __restrict__ src_head, int kv0,
-                                                 int N, int wave, int lane) {
+__device__ __forceinline__ void load_tile_part(char* smem, int buf_off,
+                                               const uint16_t* __restrict__ src_head, int kv0,
+                                               int N, int wave, int lane, int r) {
   using Lay = Bf16Layout<D>;
-#pragma unroll
-  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
+  {
     const int slice = wave * Lay::kLoadsPerWave + r;
     int row, col;
     if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
@@ -180,15 +184,31 @@ __device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
   }
 }
 
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
+                                                 const uint16_t* __restrict__ src_head, int kv0,
+                                                 int N, int wave, int lane) {
+#pragma unroll
+  for (int r = 0; r < Bf16Layout<D>::kLoadsPerWave; ++r)
+    load_tile_part<D, IS_V>(smem, buf_off, src_head, kv0, N, wave, lane, r);
+}
+
 // Scores of one tile, transposed: sacc[kb] = K[32kb + key_of_row(.)] Q^T.
 // kaddr = LDS address of this lane's K piece in slab 0, block 0: row
 // key_of_row(qi), half hh (swapped by the row's bit 3); slab s and block kb add
 // constants.  The operand reads run kAhead MFMAs ahead of their use, in a
 // rotation of kAhead + 2 register slots (a slot is refilled two MFMAs after
-// the one that read it).
-template <int D, int kAhead = 6>
+// the one that read it).  work(i) (VALU work given as an integral constant
+// index) follows MFMA i, and a scheduling barrier closes each such chunk, so
+// the program order of MFMAs and VALU work is the one written here.
+struct NoWork {
+  template <typename I>
+  __device__ __forceinline__ void operator()(I) const {}
+};
+
+template <int D, int kAhead = 6, typename Work = NoWork>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D / 16],
-                                           f32x16 (&sacc)[2]) {
+                                           f32x16 (&sacc)[2], Work&& work = Work{}) {
   using Lay = Bf16Layout<D>;
   constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
   constexpr int kSlots = kAhead + 2;
@@ -211,6 +231,8 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D 
     pin(a[i % kSlots]);
     sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i % kSlots]),
                                                          qf[i / 2], sacc[i % 2], 0, 0, 0);
+    work(ic);
+    __builtin_amdgcn_sched_barrier(0);
   });
 }
 
@@ -219,9 +241,9 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D 
 // where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2) [+ 4 for the
 // second read]; the transpose hands lane i the column d0 + i.  vaddr = LDS
 // address of this lane's piece in slab 0, step 0, first read.
-template <int D, int kAhead = 4>
+template <int D, int kAhead = 4, typename Work = NoWork>
 __device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN / 16],
-                                        f32x16 (&oacc)[D / 32]) {
+                                        f32x16 (&oacc)[D / 32], Work&& work = Work{}) {
   using Lay = Bf16Layout<D>;
   constexpr int kBlocks = D / 32;
   constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
@@ -250,6 +272,8 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN /
     const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[s],
                                                        oacc[db], 0, 0, 0);
+    work(ic);
+    __builtin_amdgcn_sched_barrier(0);
   });
 }
 
@@ -390,53 +414,79 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
         }
     }
   };
-  auto stage1 = [&](f32x16(&sc)[2], float& alpha, bool& need, float& half_sum) {
+  // The softmax of a tile as numbered steps, so that each MFMA of a phase can
+  // be given its share (step s of NS goes after MFMA s * kMf / NS).
+  // Stage 1 (18 steps): the eight partial maxima, the row maximum and the
+  // reference update, eight pairs of exponentials of block 0, their sum.
+  // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
+  // into l_run, eight pairs of bf16 conversions into the P^T operands.
+  struct SoftmaxState {
     float m8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kb = i >> 2, e = 4 * (i & 3);
-      m8[i] = fmaxf(fmaxf(sc[kb][e], sc[kb][e + 1]), fmaxf(sc[kb][e + 2], sc[kb][e + 3]));
-    }
-    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                     fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-    mx = max_halves(mx);
-    const float cand = mx * scale_log2;  // -inf for a fully masked tile
-    need = cand > base_run + kTau;
-    const float base_new = need ? cand : base_run;
-    alpha = fast_exp2(base_run - base_new);
-    m_ref = need ? mx : m_ref;
-    base_run = base_new;
-    float ps[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p[u] = fast_exp2(__builtin_fmaf(sc[0][4 * i + u], scale_log2, -base_run));
-        sc[0][4 * i + u] = p[u];
-      }
-      ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
-    }
-    half_sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    float alpha, half_sum;
+    bool need;
   };
-  auto stage2 = [&](f32x16(&sc)[2], float alpha, float half_sum, bf16x8(&pfo)[kBN / 16]) {
-    float ps[4];
+  constexpr int kStage1Steps = 18, kStage2Steps = 17;
+  auto stage1_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st) {
+    constexpr int sidx = decltype(sic)::value;
+    if constexpr (sidx < 8) {
+      constexpr int kb = sidx >> 2, e = 4 * (sidx & 3);
+      st.m8[sidx] = fmaxf(fmaxf(sc[kb][e], sc[kb][e + 1]), fmaxf(sc[kb][e + 2], sc[kb][e + 3]));
+    } else if constexpr (sidx == 8) {
+      float mx = fmaxf(fmaxf(fmaxf(st.m8[0], st.m8[1]), fmaxf(st.m8[2], st.m8[3])),
+                       fmaxf(fmaxf(st.m8[4], st.m8[5]), fmaxf(st.m8[6], st.m8[7])));
+      mx = max_halves(mx);
+      const float cand = mx * scale_log2;  // -inf for a fully masked tile
+      st.need = cand > base_run + kTau;
+      const float base_new = st.need ? cand : base_run;
+      st.alpha = fast_exp2(base_run - base_new);
+      m_ref = st.need ? mx : m_ref;
+      base_run = base_new;
+    } else if constexpr (sidx < 17) {
+      constexpr int e = 2 * (sidx - 9);
+      sc[0][e] = fast_exp2(__builtin_fmaf(sc[0][e], scale_log2, -base_run));
+      sc[0][e + 1] = fast_exp2(__builtin_fmaf(sc[0][e + 1], scale_log2, -base_run));
+    } else {
+      float q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p[u] = fast_exp2(__builtin_fmaf(sc[1][4 * i + u], scale_log2, -base_run));
-        sc[1][4 * i + u] = p[u];
-      }
-      ps[i] = (p[0] + p[1]) + (p[2] + p[3]);
+      for (int i = 0; i < 8; ++i) q[i] = sc[0][2 * i] + sc[0][2 * i + 1];
+      st.half_sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
     }
-    const float lsum = half_sum + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    l_run = __builtin_fmaf(l_run, alpha, lsum);
+  };
+  auto stage2_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st, bf16x8(&pfo)[kBN / 16]) {
+    constexpr int sidx = decltype(sic)::value;
+    if constexpr (sidx < 8) {
+      constexpr int e = 2 * sidx;
+      sc[1][e] = fast_exp2(__builtin_fmaf(sc[1][e], scale_log2, -base_run));
+      sc[1][e + 1] = fast_exp2(__builtin_fmaf(sc[1][e + 1], scale_log2, -base_run));
+    } else if constexpr (sidx == 8) {
+      float q[8];
 #pragma unroll
-    for (int s2 = 0; s2 < kBN / 16; ++s2)
+      for (int i = 0; i < 8; ++i) q[i] = sc[1][2 * i] + sc[1][2 * i + 1];
+      const float lsum =
+          st.half_sum + (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+      l_run = __builtin_fmaf(l_run, st.alpha, lsum);
+    } else {
+      // pair k of the 32 conversions: elements 4k .. 4k+3 of the tile's keys
+      constexpr int k = sidx - 9;
+      constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pfo[s2][j] = (__bf16)sc[s2 >> 1][8 * (s2 & 1) + j];
+      for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (__bf16)sc[s2 >> 1][8 * (s2 & 1) + j];
+    }
+  };
+  // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
+  auto run_steps = [&](auto ic, auto nsteps_ic, auto&& step) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int NS = decltype(nsteps_ic)::value;
+    static_for<NS>([&](auto sic) {
+      constexpr int sidx = decltype(sic)::value;
+      if constexpr (sidx * kMf / NS == i) step(sic);
+    });
+  };
+  auto stage1 = [&](f32x16(&sc)[2], SoftmaxState& st) {
+    static_for<kStage1Steps>([&](auto sic) { stage1_step(sic, sc, st); });
+  };
+  auto stage2 = [&](f32x16(&sc)[2], SoftmaxState& st, bf16x8(&pfo)[kBN / 16]) {
+    static_for<kStage2Steps>([&](auto sic) { stage2_step(sic, sc, st, pfo); });
   };
   // Empty asm that ties values to this point of the program: the compiler
   // would otherwise sink them past the next branch, next to their use.
@@ -464,16 +514,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     asm volatile("" : "+v"(l_run));
   };
 
-  // Prologue.  Ring slots: tile j lives in slot j % 3 of its ring.  Iteration
-  // t reads V_t and K_{t+2} and refills the slots of V_{t-1} and K_{t+1} with
-  // V_{t+2} and K_{t+4}; so before iteration 0, K_0..K_2 and V_0 must have
-  // landed and K_3, V_1 be in flight.
+  // Prologue.  Ring slots: tile j lives in slot j % kStages of its ring.
+  // Iteration t reads V_t and K_{t+2} and refills the slots of K_{t+1} and
+  // V_{t-1} (read in iteration t-1) with K_{t+1+S} and V_{t-1+S}, S =
+  // kStages.  Before iteration 0, K_0..K_2 and V_0 must have landed; the
+  // loads of the "iterations" 2-S .. -1 are issued here in loop order so
+  // that the vmcnt at the end of every iteration stays exact.  K_S goes to
+  // the slot of K_0, which the prologue's scores read, so it waits for the
+  // second barrier.
   load_k(0, 0);
   load_k(1, 1);
   load_k(2, 2);
   load_v(0, 0);
-  load_v(1, 1);
-  wait_vmcnt<kVmPerTile>();  // all but V_1
+#pragma unroll
+  for (int j = 3; j < kStages; ++j) {
+    load_k(j, j);
+    load_v(j - 2, j - 2);
+  }
+  load_v(kStages - 2, kStages - 2);
+  wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
   block_sync();
 
   f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
@@ -482,73 +541,72 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     score_tile<D>(k_addr(0), qf, sA);
     score_tile<D>(k_addr(1), qf, sB);
     mask_tile(0, sA);
-    float alpha, hs;
-    bool need;
-    stage1(sA, alpha, need, hs);
-    stage2(sA, alpha, hs, pf);
+    SoftmaxState st;
+    stage1(sA, st);
+    stage2(sA, st, pf);
   }
   block_sync();  // every wave is done reading K_0 before its slot is refilled
-  load_k(0, 3);
+  load_k(0, kStages);
 
-  // One tile.  Slots: a = t % 3, b = (t+1) % 3, c = (t+2) % 3.  On entry pf
-  // holds P_t and cur the raw scores of tile t+1; nxt receives tile t+2.
-  auto iteration = [&](int t, int a, int b, int c, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-    load_k(b, t + 4);
-    load_v(c, t + 2);
-
+  // One tile.  Slot sv = t % S holds V_t; K_{t+2} is in slot (t+2) % S.  On
+  // entry pf holds P_t and cur the raw scores of tile t+1; nxt receives tile
+  // t+2.
+  auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
+  // The loads of later tiles (K_{t+1+S} and V_{t-1+S}, into slots freed by
+  // the previous barrier) are issued inside the two MFMA phases rather than
+  // all at the top: eight waves issuing them at once right after the barrier
+  // queue up in the address unit.
+  auto iteration = [&](int t, int sv, f32x16(&cur)[2], f32x16(&nxt)[2]) {
     if (t + 1 < my_tiles) {
       mask_tile(t + 1, cur);
-      // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU).
-      pv_tile<D>(v_addr(a), pf, oacc);
-      float alpha, hs;
-      bool need;
-      stage1(cur, alpha, need, hs);
-#pragma unroll
-      for (int i = 0; i < kMf; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-      }
+      // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
+      // the K load of a later tile in the middle.
+      SoftmaxState st;
+      pv_tile<D>(v_addr(sv), pf, oacc, [&](auto ic) {
+        run_steps(ic, std::integral_constant<int, kStage1Steps>{},
+                  [&](auto sic) { stage1_step(sic, cur, st); });
+        if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sv + 1), t + 1 + kStages);
+      });
       pin_scores(cur);
-      asm volatile("" : "+v"(hs), "+v"(alpha));
+      asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
 
       // Phase 2: move the output to the new reference (rare).
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
       }
 
-      // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU).
-      score_tile<D>(k_addr(c), qf, nxt);
-      stage2(cur, alpha, hs, pf);
-#pragma unroll
-      for (int i = 0; i < kMf; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
-      }
+      // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
+      // with the V load of a later tile in the middle.
+      score_tile<D>(k_addr(wrap(sv + 2)), qf, nxt, [&](auto ic) {
+        run_steps(ic, std::integral_constant<int, kStage2Steps>{},
+                  [&](auto sic) { stage2_step(sic, cur, st, pf); });
+        if constexpr (decltype(ic)::value == kMf / 2)
+          load_v(wrap(sv + kStages - 1), t - 1 + kStages);
+      });
       pin_probs(pf);
-    } else if (t < my_tiles) {
-      pv_tile<D>(v_addr(a), pf, oacc);
+    } else {
+      load_k(wrap(sv + 1), t + 1 + kStages);
+      if (t < my_tiles) pv_tile<D>(v_addr(sv), pf, oacc);
+      load_v(wrap(sv + kStages - 1), t - 1 + kStages);
     }
 
-    // K_{t+3} and V_{t+1} (issued one iteration earlier) must have landed for
-    // every wave before anyone reads them; this iteration's loads may stay in
-    // flight.
-    wait_vmcnt<2 * kVmPerTile>();
+    // K_{t+3} and V_{t+1} (issued in iteration t+2-S) must have landed for
+    // every wave before anyone reads them; the loads of the S-2 later
+    // iterations may stay in flight.
+    wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
     block_sync();
   };
 
   // Two tiles per trip so that the two score buffers swap roles instead of
   // being copied.
-  int t = 0, a = 0, b = 1, c = 2;
+  int t = 0, sv = 0;
   for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, a, b, c, sB, sA);
-    iteration(t + 1, b, c, a, sA, sB);
-    const int a2 = c, b2 = a, c2 = b;  // slots advance by two
-    a = a2;
-    b = b2;
-    c = c2;
+    iteration(t, sv, sB, sA);
+    iteration(t + 1, wrap(sv + 1), sA, sB);
+    sv = wrap(sv + 2);
   }
-  if (t < n_tiles) iteration(t, a, b, c, sB, sA);
+  if (t < n_tiles) iteration(t, sv, sB, sA);
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
   const float l_tot = sum_halves(l_run);
