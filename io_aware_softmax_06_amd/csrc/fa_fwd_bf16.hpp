@@ -295,9 +295,11 @@ __device__ __forceinline__ float sum_halves(float v) {
 // ids round-robin over its 8 XCDs, each with its own L2.  Every XCD gets
 // whole heads, so the query tiles of a head share one L2 for their repeated
 // reads of that head's K and V.  Causal tiles differ in work (tile i streams
-// i+1 blocks of keys): within an XCD the ids then run longest tile first over
-// all of the XCD's heads, the longest-processing-time-first order that keeps
-// the XCD's CUs evenly loaded to the end.
+// i+1 blocks of keys): within an XCD the heads are taken two at a time, and
+// the tiles of each pair run longest first (longest-processing-time order,
+// which keeps the XCD's CUs evenly loaded to the end).  Pairs rather than all
+// of the XCD's heads at once keep the K and V being streamed near the size of
+// the L2 instead of re-fetching them from beyond it.
 template <bool CAUSAL>
 __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& qt) {
   constexpr int kXcds = 8;
@@ -305,8 +307,10 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& 
     const int hp = BH / kXcds;            // heads per XCD
     const int xcd = bid % kXcds, slot = bid / kXcds;
     if (CAUSAL) {
-      qt = nq - 1 - slot / hp;
-      bh = xcd * hp + slot % hp;
+      const int G = hp % 2 == 0 ? 2 : 1;  // heads per longest-first group
+      const int grp = slot / (G * nq), r = slot % (G * nq);
+      qt = nq - 1 - r / G;
+      bh = xcd * hp + grp * G + r % G;
     } else {
       bh = xcd * hp + slot / nq;
       qt = slot % nq;
