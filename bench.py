@@ -2,12 +2,17 @@
 """Throughput of the attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--splits S] [--no-cpu-baseline]
 
 One step is one fa_fwd call (the whole forward: QK^T, online softmax, PV,
 normalisation, O and L written) over one batch of seeded synthetic inputs
 already resident in device memory.  The default workload is the causal bf16
 case B=2, H=32, N=4096, d=128, on which the MFMA-peak target is stated.
+
+For the key-range split workloads (few query tiles per head) a step is one
+fa_fwd_splitkv call instead: the split kernel and the merge kernel, with the
+workspace allocated before the timed region.  The line then also carries the
+unsplit fa_fwd time on the same inputs for comparison (`unsplit`).
 
 Prints ONE JSON line.  `value` is attention TFLOP/s with the conventional
 count 4*B*H*N^2*d (halved for causal) over the timed steps' wall time.
@@ -113,6 +118,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--splits", type=int, default=0,
+                    help="key ranges of the split path (default: the workload's own; "
+                         "0 for a workload without one runs fa_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB "
@@ -136,26 +144,53 @@ def main():
     O = torch.empty_like(q)
     L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    splits = args.splits or workloads.SPLITS_OF.get(w.name, 0)
+    ws = None
+    if splits:
+        need = fa.fa_fwd_splitkv_workspace(w.B, w.H, w.N, w.d, splits)
+        if need < 0:
+            raise fa.FaError(need)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-    def step():
+    def unsplit_step():
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L, stream=stream)
+
+    def split_step():
+        fa.fwd_splitkv(q, k, v, splits, scale=w.scale, causal=w.causal, out=O, lse=L,
+                       workspace=ws, stream=stream)
+
+    step = split_step if splits else unsplit_step
+
+    def timed(fn, n):
+        """(wall seconds, per-step event milliseconds) of n calls on `stream`."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        return wall_s, [a.elapsed_time(b) for a, b in zip(starts, ends)]
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    wall, launch_ms = timed(step, args.steps)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    unsplit = None
+    if splits:  # after the timed region: the single-pass kernel on the same inputs
+        for _ in range(max(1, args.warmup // 2)):
+            unsplit_step()
+        _, ms = timed(unsplit_step, args.steps)
+        avg = sum(ms) / len(ms) / 1e3
+        unsplit = {"kernel_us": round(avg * 1e6, 2),
+                   "tflops": round(attention_flops(w) / avg / 1e12, 3),
+                   "split_speedup": round(avg / avg_launch_s, 3)}
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -192,7 +227,9 @@ def main():
         "data": "synthetic (seeded normal Q, K, V)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "layout": "[B,H,N,d]",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "entry_point": "fa_fwd_splitkv" if splits else "fa_fwd",
+                   **({"num_splits": splits} if splits else {})},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
@@ -201,8 +238,11 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(w.name),
+            **({"kernels": "split forward + merge (one step, both launches)"}
+               if splits else {}),
         },
         "cpu_baseline": None,
+        **({"unsplit": unsplit} if splits else {}),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.seed)

@@ -39,7 +39,9 @@ typedef enum {
   FA_ERR_ALIGN = -6,          /* Q, K, V or O not 16-byte aligned, or L not 4-byte aligned */
   FA_ERR_ALIAS = -7,          /* O or L overlaps an input, or O overlaps L */
   FA_ERR_HIP = -8,            /* the HIP runtime reported an error at launch */
-  FA_ERR_ARG = -9             /* causal is not 0 or 1 */
+  FA_ERR_ARG = -9,            /* causal is not 0 or 1 */
+  FA_ERR_SPLITS = -10,        /* num_splits is not in [1, 128] */
+  FA_ERR_WORKSPACE = -11      /* workspace NULL, too small or not 256-byte aligned */
 } fa_status;
 
 /*
@@ -78,6 +80,55 @@ typedef enum {
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
            int64_t B, int64_t H, int64_t N, int64_t d,
            float scale, int causal, void* stream, int dtype);
+
+/*
+ * Key-range split forward (for few query blocks per head, where one
+ * workgroup per query block leaves most of the chip idle).
+ *
+ * The query rows are taken in blocks of 256 (rows 256 rb .. 256 rb + 255).
+ * The keys visible to block rb -- all N, or with causal = 1 the first
+ * V_rb = min(N, 256 (rb + 1)) -- are cut into num_splits ranges on 64-key
+ * boundaries: with T_rb = ceil(V_rb / 64) tiles, range s of block rb is
+ * keys [64 floor(s T_rb / S), min(V_rb, 64 floor((s+1) T_rb / S))).  Cutting
+ * the visible keys rather than all N gives each range of a causal block the
+ * same work.  A first kernel computes, for every query row and every range s
+ * of its block, the attention of the row over that range alone: its output
+ * O_s, already divided by its own softmax denominator, and its logsumexp L_s
+ * (-inf, with O_s = 0, when no key of the range is visible to the row).  A
+ * second kernel combines the ranges with the softmax-of-a-concatenation rule
+ * (the Triton article, section "瓦片注意力计算": m = max(m1, m2),
+ * l = e^(m1-m) l1 + e^(m2-m) l2), carried over to O because O is linear in
+ * the softmax weights:
+ *     L = ln sum_s e^(L_s),     O = sum_s e^(L_s - L) O_s.
+ * The result equals fa_fwd's up to float rounding (not bitwise: the sums are
+ * grouped differently).
+ *
+ * fa_fwd_splitkv_workspace returns the workspace size in bytes,
+ * num_splits * B*H*N * (d + 1) * 4, or a negative fa_status
+ * (FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D, FA_ERR_SPLITS).  It makes no HIP call.
+ *
+ * fa_fwd_splitkv takes fa_fwd's arguments plus
+ *   num_splits       number of key ranges, 1..128; ranges beyond the number
+ *                    of key tiles are empty and cost one idle workgroup each.
+ *   workspace        device pointer, 256-byte aligned, owned by the caller,
+ *                    at least fa_fwd_splitkv_workspace(...) bytes, not
+ *                    overlapping Q, K, V, O or L.  Overwritten: float32
+ *                    O_s [num_splits][B*H*N][d] followed by float32
+ *                    L_s [num_splits][B*H*N].  Its contents after the call are
+ *                    these partials; nothing needs to be cleared before.
+ *   workspace_bytes  size of the workspace buffer.
+ * It enqueues the two kernels on `stream` and does not synchronise.  The
+ * checks and errors are fa_fwd's, plus FA_ERR_SPLITS and FA_ERR_WORKSPACE;
+ * FA_ERR_ALIAS also covers a workspace overlapping another buffer.  Two calls
+ * that share one workspace must be ordered (same stream or an event).
+ * Deterministic: identical inputs give bitwise-identical outputs.
+ */
+int64_t fa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits);
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   float scale, int causal, void* stream, int dtype,
+                   int num_splits, void* workspace, int64_t workspace_bytes);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

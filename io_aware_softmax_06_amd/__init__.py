@@ -7,12 +7,17 @@ call raises.
 
 Raw C-ABI functions (same names and argument order as include/fa355.h):
     fa_fwd(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype) -> int
+    fa_fwd_splitkv_workspace(B, H, N, d, num_splits) -> int (bytes or status)
+    fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype,
+                   num_splits, workspace, workspace_bytes) -> int
     fa_strerror(status) -> str
     fa_version() -> int
 where Q, K, V, O, L and stream are integer addresses.
 
 Tensor front end:
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (O, L)
+    fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, out=None,
+                lse=None, workspace=None) -> (O, L, workspace)
 """
 
 import ctypes
@@ -35,6 +40,8 @@ FA_ERR_ALIGN = -6
 FA_ERR_ALIAS = -7
 FA_ERR_HIP = -8
 FA_ERR_ARG = -9
+FA_ERR_SPLITS = -10
+FA_ERR_WORKSPACE = -11
 
 _lib = None
 
@@ -61,6 +68,12 @@ def load(path=LIB_PATH):
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, vp, ctypes.c_int]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.fa_fwd_splitkv_workspace.restype = i64
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_int, vp, ctypes.c_int,
+                                   ctypes.c_int, vp, i64]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -72,6 +85,18 @@ def load(path=LIB_PATH):
 def fa_fwd(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype):
     """Direct call of the C entry point; returns its status code."""
     return load().fa_fwd(Q, K, V, O, L, B, H, N, d, float(scale), int(causal), stream, dtype)
+
+
+def fa_fwd_splitkv_workspace(B, H, N, d, num_splits):
+    """Workspace bytes of fa_fwd_splitkv, or a negative status."""
+    return load().fa_fwd_splitkv_workspace(B, H, N, d, int(num_splits))
+
+
+def fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_splits,
+                   workspace, workspace_bytes):
+    """Direct call of the C entry point; returns its status code."""
+    return load().fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, float(scale), int(causal), stream,
+                                 dtype, int(num_splits), workspace, workspace_bytes)
 
 
 def fa_strerror(status):
@@ -91,12 +116,7 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
 
 
-def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
-    """Attention forward on [B, H, N, d] device tensors; returns (O, L).
-
-    O has q's dtype and shape; L is float32 [B, H, N].  Runs on ``stream``
-    (default: torch's current stream) and does not synchronise.
-    """
+def _prepare(q, k, v, scale, out, lse, stream):
     import torch
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -122,8 +142,57 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    return (B, H, N, d), scale, out, lse, stream
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward on [B, H, N, d] device tensors; returns (O, L).
+
+    O has q's dtype and shape; L is float32 [B, H, N].  Runs on ``stream``
+    (default: torch's current stream) and does not synchronise.
+    """
+    (B, H, N, d), scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q))
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
+
+
+def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, out=None, lse=None,
+                workspace=None, stream=None):
+    """Key-range split forward; returns (O, L, workspace).
+
+    Same result as ``fwd`` up to float rounding.  ``workspace`` is a uint8
+    device tensor of at least ``fa_fwd_splitkv_workspace(...)`` bytes
+    (allocated here when None); after the call it holds the per-range
+    partials O_s float32 [num_splits, B, H, N, d] followed by L_s float32
+    [num_splits, B, H, N].
+    """
+    import torch
+    (B, H, N, d), scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
+    need = fa_fwd_splitkv_workspace(B, H, N, d, num_splits)
+    if need < 0:
+        raise FaError(need)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                        stream.cuda_stream, _dtype_code(q), num_splits, workspace.data_ptr(),
+                        ws_bytes)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse, workspace
+
+
+def split_partials(workspace, num_splits, B, H, N, d):
+    """Views (O_s [S, B, H, N, d], L_s [S, B, H, N]) of a split workspace."""
+    import torch
+    rows = B * H * N
+    f = workspace[: num_splits * rows * (d + 1) * 4].view(torch.float32)
+    o = f[: num_splits * rows * d].view(num_splits, B, H, N, d)
+    l = f[num_splits * rows * d:].view(num_splits, B, H, N)
+    return o, l

@@ -13,59 +13,29 @@
 
 #include "fa_fwd_bf16.hpp"
 #include "fa_fwd_f32.hpp"
+#include "fa_merge.hpp"
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: key-range split forward and merge
+constexpr int kMaxSplits = 128;
 
 bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
   return pa < pb + nb && pb < pa + na;
 }
 
-// The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
-// instance's limit once per process (device-independent attribute).
-template <int D, bool CAUSAL>
-hipError_t prepare_bf16() {
-  static const hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::Bf16Layout<D>::kBytes);
-  return status;
-}
+// Sizes derived from a validated call.
+struct Sizes {
+  int64_t BH;
+  uint64_t rows;          // B*H*N
+  uint64_t tensor_bytes;  // one of Q, K, V, O
+  uint64_t lse_bytes;     // L
+};
 
-template <int D, bool CAUSAL>
-hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
-                       int64_t BH, int64_t N, float scale, hipStream_t stream) {
-  const hipError_t prep = prepare_bf16<D, CAUSAL>();
-  if (prep != hipSuccess) return prep;
-  const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
-  const int total = (int)(BH * num_qtiles);
-  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(fa355::kThreads),
-                     fa355::Bf16Layout<D>::kBytes, stream, static_cast<const uint16_t*>(Q),
-                     static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
-                     static_cast<uint16_t*>(O), L, (int)N, (int)BH, num_qtiles, scale,
-                     scale * fa355::kLog2e);
-  return hipGetLastError();
-}
-
-template <int D, bool CAUSAL>
-hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
-                int64_t N, float scale, hipStream_t stream) {
-  constexpr int kRows = 64 / (D / 64);
-  const int num_qtiles = (int)((N + kRows - 1) / kRows);
-  const int total = (int)(BH * num_qtiles);
-  hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL>), dim3(total), dim3(64), 0, stream,
-                     static_cast<const float*>(Q), static_cast<const float*>(K),
-                     static_cast<const float*>(V), static_cast<float*>(O), L, (int)N, num_qtiles,
-                     scale, scale * fa355::kLog2e);
-  return hipGetLastError();
-}
-
-}  // namespace
-
-extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
-                      int64_t H, int64_t N, int64_t d, float scale, int causal, void* stream,
-                      int dtype) {
+// Every check of fa_fwd, before any HIP call.  Returns FA_OK or the status.
+int check_args(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
+               int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, Sizes* sz) {
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
@@ -95,24 +65,152 @@ extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, floa
     if (ranges_overlap(L, lse_bytes, in, tensor_bytes)) return FA_ERR_ALIAS;
   }
   if (ranges_overlap(L, lse_bytes, O, tensor_bytes)) return FA_ERR_ALIAS;
+  *sz = {BH, rows, tensor_bytes, lse_bytes};
+  return FA_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
-  hipError_t err;
+// Workspace of the split forward: O_s (float32 [S][rows][d]) then L_s
+// (float32 [S][rows]).  0 if the size does not fit 64 bits.
+uint64_t split_workspace_bytes(uint64_t rows, int64_t d, int splits) {
+  const uint64_t per_split = rows * ((uint64_t)d + 1) * 4;
+  if (per_split > UINT64_MAX / (uint64_t)splits) return 0;
+  return per_split * (uint64_t)splits;
+}
+
+// The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
+// instance's limit once per process (device-independent attribute).
+template <int D, bool CAUSAL, bool SPLIT>
+hipError_t prepare_bf16() {
+  static const hipError_t status = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::Bf16Layout<D>::kBytes);
+  return status;
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
+                       int64_t BH, int64_t N, float scale, fa355::SplitArgs sa,
+                       hipStream_t stream) {
+  const hipError_t prep = prepare_bf16<D, CAUSAL, SPLIT>();
+  if (prep != hipSuccess) return prep;
+  const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
+  const int total = (int)(BH * num_qtiles * sa.num_splits);
+  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(total),
+                     dim3(fa355::kThreads), fa355::Bf16Layout<D>::kBytes, stream,
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), L, (int)N,
+                     (int)BH, num_qtiles, scale, scale * fa355::kLog2e, sa);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
+                      int64_t N, float scale, fa355::SplitArgs sa, hipStream_t stream) {
+  constexpr int kRows = 64 / (D / 64);
+  const int num_qtiles = (int)((N + kRows - 1) / kRows);
+  const int total = (int)(BH * num_qtiles * sa.num_splits);
+  hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, SPLIT>), dim3(total), dim3(64), 0,
+                     stream, static_cast<const float*>(Q), static_cast<const float*>(K),
+                     static_cast<const float*>(V), static_cast<float*>(O), L, (int)N, (int)BH,
+                     num_qtiles, scale, scale * fa355::kLog2e, sa);
+  return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, float* L,
+                          int64_t BH, int64_t N, int64_t d, float scale, int causal, int dtype,
+                          fa355::SplitArgs sa, hipStream_t s) {
   if (dtype == FA_BF16) {
     if (d == 64)
-      err = causal ? launch_bf16<64, true>(Q, K, V, O, L, BH, N, scale, s)
-                   : launch_bf16<64, false>(Q, K, V, O, L, BH, N, scale, s);
+      return causal ? launch_bf16<64, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
+                    : launch_bf16<64, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+    return causal ? launch_bf16<128, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_bf16<128, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+  }
+  if (d == 64)
+    return causal ? launch_f32<64, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_f32<64, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+  return causal ? launch_f32<128, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
+                : launch_f32<128, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+}
+
+template <int D, typename OutT>
+hipError_t launch_merge(const float* opart, const float* lpart, void* O, float* L, int S,
+                        uint64_t rows, hipStream_t s) {
+  constexpr int kRowsPerBlock = fa355::kMergeThreads / (D / 4);
+  constexpr uint64_t kMaxBlocks = 1u << 20;  // the kernel strides over the rest
+  uint64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  hipLaunchKernelGGL((fa355::fa_merge_kernel<D, OutT>), dim3((unsigned)blocks),
+                     dim3(fa355::kMergeThreads), 0, s, opart, lpart, static_cast<OutT*>(O), L, S,
+                     (int64_t)rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
+                      int64_t H, int64_t N, int64_t d, float scale, int causal, void* stream,
+                      int dtype) {
+  Sizes sz;
+  const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
+  if (rc != FA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
+  const fa355::SplitArgs whole = {1, nullptr, nullptr};
+  const hipError_t err =
+      launch_forward<false>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, whole, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int64_t fa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                            int num_splits) {
+  if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
+    return FA_ERR_SHAPE;
+  if (B * H > INT_MAX) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  const uint64_t bytes = split_workspace_bytes((uint64_t)(B * H) * (uint64_t)N, d, num_splits);
+  if (bytes == 0 || bytes > (uint64_t)INT64_MAX) return FA_ERR_SHAPE;
+  return (int64_t)bytes;
+}
+
+extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
+                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                              void* stream, int dtype, int num_splits, void* workspace,
+                              int64_t workspace_bytes) {
+  Sizes sz;
+  const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  // Grid of the split pass: one workgroup per (query tile, split) of each head.
+  const int64_t min_rows_per_block = 32;
+  if (sz.BH * ((N + min_rows_per_block - 1) / min_rows_per_block) * num_splits > INT_MAX)
+    return FA_ERR_SHAPE;
+  const uint64_t need = split_workspace_bytes(sz.rows, d, num_splits);
+  if (need == 0) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < 0 || (uint64_t)workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FA_ERR_WORKSPACE;
+  for (const void* p : {Q, K, V, static_cast<const void*>(O)})
+    if (ranges_overlap(workspace, need, p, sz.tensor_bytes)) return FA_ERR_ALIAS;
+  if (ranges_overlap(workspace, need, L, sz.lse_bytes)) return FA_ERR_ALIAS;
+
+  float* opart = static_cast<float*>(workspace);
+  float* lpart = opart + sz.rows * (uint64_t)d * (uint64_t)num_splits;
+  const fa355::SplitArgs sa = {num_splits, opart, lpart};
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t err =
+      launch_forward<true>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, sa, s);
+  if (err == hipSuccess) {
+    if (dtype == FA_BF16)
+      err = d == 64 ? launch_merge<64, uint16_t>(opart, lpart, O, L, num_splits, sz.rows, s)
+                    : launch_merge<128, uint16_t>(opart, lpart, O, L, num_splits, sz.rows, s);
     else
-      err = causal ? launch_bf16<128, true>(Q, K, V, O, L, BH, N, scale, s)
-                   : launch_bf16<128, false>(Q, K, V, O, L, BH, N, scale, s);
-  } else {
-    if (d == 64)
-      err = causal ? launch_f32<64, true>(Q, K, V, O, L, BH, N, scale, s)
-                   : launch_f32<64, false>(Q, K, V, O, L, BH, N, scale, s);
-    else
-      err = causal ? launch_f32<128, true>(Q, K, V, O, L, BH, N, scale, s)
-                   : launch_f32<128, false>(Q, K, V, O, L, BH, N, scale, s);
+      err = d == 64 ? launch_merge<64, float>(opart, lpart, O, L, num_splits, sz.rows, s)
+                    : launch_merge<128, float>(opart, lpart, O, L, num_splits, sz.rows, s);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -126,9 +224,12 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_DTYPE: return "dtype must be FA_BF16 (0) or FA_F32 (1)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "Q, K, V, O must be 16-byte aligned and L 4-byte aligned";
-    case FA_ERR_ALIAS: return "O or L overlaps an input, or O overlaps L";
+    case FA_ERR_ALIAS: return "O, L or the workspace overlaps another buffer of the call";
     case FA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
     case FA_ERR_ARG: return "causal must be 0 or 1";
+    case FA_ERR_SPLITS: return "num_splits must be between 1 and 128";
+    case FA_ERR_WORKSPACE: return "workspace is NULL, smaller than fa_fwd_splitkv_workspace() "
+                                  "bytes or not 256-byte aligned";
     default: return "unknown status code";
   }
 }

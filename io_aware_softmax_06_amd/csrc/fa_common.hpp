@@ -25,4 +25,33 @@ __device__ __forceinline__ float other_half(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
+// Key-range split of the forward pass.  The query rows are grouped in blocks
+// of kSplitRows; the keys visible to block rb (all N, or with the causal mask
+// the first min(N, (rb + 1) kSplitRows)) are cut on kSplitKeys boundaries
+// into S ranges of T_rb / S tiles each (T_rb = visible keys / kSplitKeys,
+// rounded up): range s is tiles [s T_rb / S, (s+1) T_rb / S).  Cutting the
+// visible keys, not all N, gives every range of a causal block the same work.
+// With SPLIT a workgroup covers one (row block part, range) pair and writes,
+// instead of O and L, that range's partial result: the output normalised by
+// the range's own denominator, O_s (float32, [S][BH][N][d]), and the range's
+// logsumexp L_s (float32, [S][BH][N]; -inf and O_s = 0 where no key of the
+// range is visible to the row).  fa_merge_kernel combines them.
+constexpr int kSplitRows = 256;
+constexpr int kSplitKeys = 64;
+
+struct SplitArgs {
+  int num_splits;  // S (1 without SPLIT)
+  float* opart;    // O_s, SPLIT only
+  float* lpart;    // L_s, SPLIT only
+};
+
+// [lo, hi) of range s of row block rb.
+__device__ __forceinline__ void split_range(int s, int S, int rb, int N, bool causal, int& lo,
+                                            int& hi) {
+  const int visible = causal ? min(N, (rb + 1) * kSplitRows) : N;
+  const int T = (visible + kSplitKeys - 1) / kSplitKeys;
+  lo = (s * T / S) * kSplitKeys;
+  hi = min(visible, ((s + 1) * T / S) * kSplitKeys);
+}
+
 }  // namespace fa355

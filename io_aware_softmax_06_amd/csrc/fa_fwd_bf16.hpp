@@ -324,11 +324,11 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& 
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Lse, int N,
-    int BH, int num_qtiles, float scale, float scale_log2) {
+    int BH, int num_qtiles, float scale, float scale_log2, SplitArgs split_args) {
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
@@ -340,8 +340,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   const int qi = lane & 31;  // query column of this lane inside the wave's 32
   const int hh = lane >> 5;  // half-wave
 
-  int bh, qt;
-  map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
+  int bh, qt, split = 0;
+  if (SPLIT && CAUSAL) {
+    // Longest first: query tiles from the last (most visible keys) down; in
+    // each, the key ranges from the first (whole) to the ones past the
+    // diagonal (empty); heads fastest, so that consecutive workgroups, which
+    // land on different XCDs, keep each head on one XCD.
+    const int per_level = BH * split_args.num_splits;
+    const int level = blockIdx.x / per_level;
+    const int r = blockIdx.x - level * per_level;
+    split = r / BH;
+    bh = r - split * BH;
+    qt = num_qtiles - 1 - level;
+  } else if (SPLIT) {  // split index fastest, then query tile, then head
+    const int q = blockIdx.x / split_args.num_splits;
+    split = blockIdx.x - q * split_args.num_splits;
+    bh = q / num_qtiles;
+    qt = q - bh * num_qtiles;
+  } else {
+    map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
+  }
   const int q0 = qt * kBM;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qb = Q + head;
@@ -351,13 +369,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   const int wq0 = q0 + wave * 32;  // first query row of this wave
   const int qrow = wq0 + qi;
 
+  // Keys of this workgroup: [kv_lo, kv_hi) (the whole row without SPLIT).
   // Tiles the workgroup streams, and the prefix of them this wave needs.
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  static_assert(kBM == kSplitRows && kBN == kSplitKeys, "split blocks are workgroup tiles");
+  int kv_lo = 0, kv_hi = N;
+  if (SPLIT) split_range(split, split_args.num_splits, qt, N, CAUSAL, kv_lo, kv_hi);
+  const int kv_end = CAUSAL ? min(kv_hi, q0 + kBM) : kv_hi;
+  const int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
   int my_tiles = 0;
   if (wq0 < N) {
-    const int wave_end = CAUSAL ? min(N, wq0 + 32) : N;
-    my_tiles = (wave_end + kBN - 1) / kBN;
+    const int wave_end = CAUSAL ? min(kv_hi, wq0 + 32) : kv_hi;
+    my_tiles = wave_end > kv_lo ? (wave_end - kv_lo + kBN - 1) / kBN : 0;
   }
   const int last = n_tiles - 1;
 
@@ -391,12 +413,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   auto k_addr = [&](int slot) { return smem_lds + Lay::kOffK + slot * Lay::kTileBytes + k_lane; };
   auto v_addr = [&](int slot) { return smem_lds + Lay::kOffV + slot * Lay::kTileBytes + v_lane; };
   auto load_k = [&](int slot, int tile) {
-    load_tile_direct<D, false>(smem, Lay::kOffK + slot * Lay::kTileBytes, Kb, min(tile, last) * kBN,
-                               N, wave, lane);
+    load_tile_direct<D, false>(smem, Lay::kOffK + slot * Lay::kTileBytes, Kb,
+                               kv_lo + min(tile, last) * kBN, N, wave, lane);
   };
   auto load_v = [&](int slot, int tile) {
-    load_tile_direct<D, true>(smem, Lay::kOffV + slot * Lay::kTileBytes, Vb, min(tile, last) * kBN,
-                              N, wave, lane);
+    load_tile_direct<D, true>(smem, Lay::kOffV + slot * Lay::kTileBytes, Vb,
+                              kv_lo + min(tile, last) * kBN, N, wave, lane);
   };
 
   // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
@@ -406,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
   // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
   auto mask_tile = [&](int j, f32x16(&sc)[2]) {
-    const int kv0 = j * kBN;
+    const int kv0 = kv_lo + j * kBN;
     const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
@@ -518,122 +540,138 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     asm volatile("" : "+v"(l_run));
   };
 
-  // Prologue.  Ring slots: tile j lives in slot j % kStages of its ring.
-  // Iteration t reads V_t and K_{t+2} and refills the slots of K_{t+1} and
-  // V_{t-1} (read in iteration t-1) with K_{t+1+S} and V_{t-1+S}, S =
-  // kStages.  Before iteration 0, K_0..K_2 and V_0 must have landed; the
-  // loads of the "iterations" 2-S .. -1 are issued here in loop order so
-  // that the vmcnt at the end of every iteration stays exact.  K_S goes to
-  // the slot of K_0, which the prologue's scores read, so it waits for the
-  // second barrier.
-  load_k(0, 0);
-  load_k(1, 1);
-  load_k(2, 2);
-  load_v(0, 0);
-#pragma unroll
-  for (int j = 3; j < kStages; ++j) {
-    load_k(j, j);
-    load_v(j - 2, j - 2);
-  }
-  load_v(kStages - 2, kStages - 2);
-  wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
-  block_sync();
+  // A workgroup whose key range is empty (a split past the causal diagonal)
+  // skips straight to the epilogue, which then writes L = -inf and O = 0.
+  if (n_tiles > 0) {
+    // Prologue.  Ring slots: tile j lives in slot j % kStages of its ring.
+    // Iteration t reads V_t and K_{t+2} and refills the slots of K_{t+1} and
+    // V_{t-1} (read in iteration t-1) with K_{t+1+S} and V_{t-1+S}, S =
+    // kStages.  Before iteration 0, K_0..K_2 and V_0 must have landed; the
+    // loads of the "iterations" 2-S .. -1 are issued here in loop order so
+    // that the vmcnt at the end of every iteration stays exact.  K_S goes to
+    // the slot of K_0, which the prologue's scores read, so it waits for the
+    // second barrier.
+    load_k(0, 0);
+    load_k(1, 1);
+    load_k(2, 2);
+    load_v(0, 0);
+  #pragma unroll
+    for (int j = 3; j < kStages; ++j) {
+      load_k(j, j);
+      load_v(j - 2, j - 2);
+    }
+    load_v(kStages - 2, kStages - 2);
+    wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
+    block_sync();
 
-  f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
-  bf16x8 pf[kBN / 16];  // P^T of the tile whose P V is next
-  if (my_tiles > 0) {
-    score_tile<D>(k_addr(0), qf, sA);
-    score_tile<D>(k_addr(1), qf, sB);
-    mask_tile(0, sA);
-    SoftmaxState st;
-    stage1(sA, st);
-    stage2(sA, st, pf);
-  }
-  block_sync();  // every wave is done reading K_0 before its slot is refilled
-  load_k(0, kStages);
-
-  // One tile.  Slot sv = t % S holds V_t; K_{t+2} is in slot (t+2) % S.  On
-  // entry pf holds P_t and cur the raw scores of tile t+1; nxt receives tile
-  // t+2.
-  auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
-  // The loads of later tiles (K_{t+1+S} and V_{t-1+S}, into slots freed by
-  // the previous barrier) are issued inside the two MFMA phases rather than
-  // all at the top: eight waves issuing them at once right after the barrier
-  // queue up in the address unit.
-  auto iteration = [&](int t, int sv, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-    if (t + 1 < my_tiles) {
-      mask_tile(t + 1, cur);
-      // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
-      // the K load of a later tile in the middle.
+    f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
+    bf16x8 pf[kBN / 16];  // P^T of the tile whose P V is next
+    if (my_tiles > 0) {
+      score_tile<D>(k_addr(0), qf, sA);
+      score_tile<D>(k_addr(1), qf, sB);
+      mask_tile(0, sA);
       SoftmaxState st;
-      pv_tile<D>(v_addr(sv), pf, oacc, [&](auto ic) {
-        run_steps(ic, std::integral_constant<int, kStage1Steps>{},
-                  [&](auto sic) { stage1_step(sic, cur, st); });
-        if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sv + 1), t + 1 + kStages);
-      });
-      pin_scores(cur);
-      asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
+      stage1(sA, st);
+      stage2(sA, st, pf);
+    }
+    block_sync();  // every wave is done reading K_0 before its slot is refilled
+    load_k(0, kStages);
 
-      // Phase 2: move the output to the new reference (rare).
-      if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
+    // One tile.  Slot sv = t % S holds V_t; K_{t+2} is in slot (t+2) % S.  On
+    // entry pf holds P_t and cur the raw scores of tile t+1; nxt receives tile
+    // t+2.
+    auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
+    // The loads of later tiles (K_{t+1+S} and V_{t-1+S}, into slots freed by
+    // the previous barrier) are issued inside the two MFMA phases rather than
+    // all at the top: eight waves issuing them at once right after the barrier
+    // queue up in the address unit.
+    auto iteration = [&](int t, int sv, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+      if (t + 1 < my_tiles) {
+        mask_tile(t + 1, cur);
+        // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
+        // the K load of a later tile in the middle.
+        SoftmaxState st;
+        pv_tile<D>(v_addr(sv), pf, oacc, [&](auto ic) {
+          run_steps(ic, std::integral_constant<int, kStage1Steps>{},
+                    [&](auto sic) { stage1_step(sic, cur, st); });
+          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sv + 1), t + 1 + kStages);
+        });
+        pin_scores(cur);
+        asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
+
+        // Phase 2: move the output to the new reference (rare).
+        if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
+  #pragma unroll
+          for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
+        }
+
+        // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
+        // with the V load of a later tile in the middle.
+        score_tile<D>(k_addr(wrap(sv + 2)), qf, nxt, [&](auto ic) {
+          run_steps(ic, std::integral_constant<int, kStage2Steps>{},
+                    [&](auto sic) { stage2_step(sic, cur, st, pf); });
+          if constexpr (decltype(ic)::value == kMf / 2)
+            load_v(wrap(sv + kStages - 1), t - 1 + kStages);
+        });
+        pin_probs(pf);
+      } else {
+        load_k(wrap(sv + 1), t + 1 + kStages);
+        if (t < my_tiles) pv_tile<D>(v_addr(sv), pf, oacc);
+        load_v(wrap(sv + kStages - 1), t - 1 + kStages);
       }
 
-      // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
-      // with the V load of a later tile in the middle.
-      score_tile<D>(k_addr(wrap(sv + 2)), qf, nxt, [&](auto ic) {
-        run_steps(ic, std::integral_constant<int, kStage2Steps>{},
-                  [&](auto sic) { stage2_step(sic, cur, st, pf); });
-        if constexpr (decltype(ic)::value == kMf / 2)
-          load_v(wrap(sv + kStages - 1), t - 1 + kStages);
-      });
-      pin_probs(pf);
-    } else {
-      load_k(wrap(sv + 1), t + 1 + kStages);
-      if (t < my_tiles) pv_tile<D>(v_addr(sv), pf, oacc);
-      load_v(wrap(sv + kStages - 1), t - 1 + kStages);
+      // K_{t+3} and V_{t+1} (issued in iteration t+2-S) must have landed for
+      // every wave before anyone reads them; the loads of the S-2 later
+      // iterations may stay in flight.
+      wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
+      block_sync();
+    };
+
+    // Two tiles per trip so that the two score buffers swap roles instead of
+    // being copied.
+    int t = 0, sv = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      iteration(t, sv, sB, sA);
+      iteration(t + 1, wrap(sv + 1), sA, sB);
+      sv = wrap(sv + 2);
     }
-
-    // K_{t+3} and V_{t+1} (issued in iteration t+2-S) must have landed for
-    // every wave before anyone reads them; the loads of the S-2 later
-    // iterations may stay in flight.
-    wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
-    block_sync();
-  };
-
-  // Two tiles per trip so that the two score buffers swap roles instead of
-  // being copied.
-  int t = 0, sv = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, sv, sB, sA);
-    iteration(t + 1, wrap(sv + 1), sA, sB);
-    sv = wrap(sv + 2);
+    if (t < n_tiles) iteration(t, sv, sB, sA);
   }
-  if (t < n_tiles) iteration(t, sv, sB, sA);
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // l_tot = sum_j exp2(s_j c - base_run) with base_run = m_ref c - r, where r
+  // (exact, from one FMA) is the rounding residual of base_run; hence
+  // ln sum_j exp(scale s_j) = m_ref scale + ln l_tot - r ln 2.
+  const float lse = l_tot > 0.f ? __builtin_fmaf(m_ref, scale, logf(l_tot) - __builtin_fmaf(m_ref, scale_log2, -base_run) * kLn2) : kNegInf;
   if (qrow < N) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
+    if (SPLIT) {
+      const size_t prow = ((size_t)split * BH + bh) * N + qrow;
+      float* orow = split_args.opart + prow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        __bf16 o4[4];
+        for (int g = 0; g < 4; ++g) {
+          f32x4 o4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(oacc[db][4 * g + r] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
-            __builtin_bit_cast(u32x2, o4);
-      }
-    if (hh == 0) {
-      // l_tot = sum_j exp2(s_j c - base_run) with base_run = m_ref c - r, where
-      // r (exact, from one FMA) is the rounding residual of base_run; hence
-      // ln sum_j exp(scale s_j) = m_ref scale + ln l_tot - r ln 2.
-      const float r = __builtin_fmaf(m_ref, scale_log2, -base_run);
-      Lse[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? __builtin_fmaf(m_ref, scale, logf(l_tot) - r * kLn2) : kNegInf;
+          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][4 * g + r] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) = o4;
+        }
+      if (hh == 0) split_args.lpart[prow] = lse;
+    } else {
+      uint16_t* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __bf16 o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(oacc[db][4 * g + r] * inv);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
+              __builtin_bit_cast(u32x2, o4);
+        }
+      if (hh == 0) Lse[(size_t)bh * N + qrow] = lse;
     }
   }
 }

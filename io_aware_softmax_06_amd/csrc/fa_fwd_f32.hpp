@@ -5,6 +5,8 @@
 // row per lane (two lanes per row when d = 128, each holding 64 of the d
 // components), 32-key tiles of K and V staged in LDS and read as broadcasts.
 // This is the exact-precision variant; bf16 inputs take the MFMA kernel.
+// With SPLIT the workgroup covers the key range of one split and writes the
+// partial result described at SplitArgs (fa_common.hpp) instead of O, L.
 #pragma once
 
 #include "fa_common.hpp"
@@ -13,11 +15,11 @@ namespace fa355 {
 
 constexpr int kF32Keys = 32;  // keys per staged tile
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ Lse, int N, int num_qtiles, float scale,
-    float scale_log2) {
+    float* __restrict__ O, float* __restrict__ Lse, int N, int BH, int num_qtiles, float scale,
+    float scale_log2, SplitArgs split_args) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int kLanesPerRow = D / 64;
   constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
@@ -27,8 +29,13 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
 
   const int lane = threadIdx.x;
   const int part = lane / kRows;  // which 64 components of d (0 when d = 64)
-  const int bh = blockIdx.x / num_qtiles;
-  int qt = blockIdx.x - bh * num_qtiles;
+  int split = 0, wg = blockIdx.x;
+  if (SPLIT) {
+    split = wg % split_args.num_splits;
+    wg /= split_args.num_splits;
+  }
+  const int bh = wg / num_qtiles;
+  int qt = wg - bh * num_qtiles;
   if (CAUSAL) qt = num_qtiles - 1 - qt;
   const int q0 = qt * kRows;
   const int qrow = q0 + lane % kRows;
@@ -47,14 +54,19 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
   // rounded so that exp2(base_old - base_new) rescales exactly.
   float m_run = kNegInf, base_run = kNegInf, l_run = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += kF32Keys) {
+  // Keys of this workgroup: [kv_lo, kv_hi), the range of its split for its
+  // 256-row block (kRows divides 256, so the workgroup lies in one block).
+  static_assert(kSplitRows % kRows == 0, "row blocks");
+  int kv_lo = 0, kv_hi = N;
+  if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
+  const int kv_end = CAUSAL ? min(kv_hi, q0 + kRows) : kv_hi;
+  for (int kv0 = kv_lo; kv0 < kv_end; kv0 += kF32Keys) {
     __syncthreads();
     for (int c = lane; c < kF32Keys * (D / 4); c += 64) {
       const int row = c / (D / 4), col = c % (D / 4);
       const int key = kv0 + row;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < N) {
+      if (key < kv_end) {
         kv = *reinterpret_cast<const f32x4*>(K + head + (size_t)key * D + 4 * col);
         vv = *reinterpret_cast<const f32x4*>(V + head + (size_t)key * D + 4 * col);
       }
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
       }
       if (kLanesPerRow == 2) acc += other_half(acc);
       const int key = kv0 + j;
-      s[j] = (key >= N || (CAUSAL && key > qrow)) ? kNegInf : acc;
+      s[j] = (key >= kv_end || (CAUSAL && key > qrow)) ? kNegInf : acc;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -106,14 +118,22 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
 
   if (qrow < N) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float r = __builtin_fmaf(m_run, scale_log2, -base_run);  // exact residual
+    const float lse = l_run > 0.f ? __builtin_fmaf(m_run, scale, logf(l_run) - r * kLn2) : kNegInf;
+    float* orow;
+    float* lrow;
+    if (SPLIT) {
+      const size_t prow = ((size_t)split * BH + bh) * N + qrow;
+      orow = split_args.opart + prow * D;
+      lrow = split_args.lpart + prow;
+    } else {
+      orow = O + head + (size_t)qrow * D;
+      lrow = Lse + (size_t)bh * N + qrow;
+    }
 #pragma unroll
     for (int t = 0; t < kDl / 4; ++t)
-      *reinterpret_cast<f32x4*>(O + head + (size_t)qrow * D + part * kDl + 4 * t) = o[t] * inv;
-    if (part == 0) {
-      const float r = __builtin_fmaf(m_run, scale_log2, -base_run);  // exact residual
-      Lse[(size_t)bh * N + qrow] =
-          l_run > 0.f ? __builtin_fmaf(m_run, scale, logf(l_run) - r * kLn2) : kNegInf;
-    }
+      *reinterpret_cast<f32x4*>(orow + part * kDl + 4 * t) = o[t] * inv;
+    if (part == 0) *lrow = lse;
   }
 }
 

@@ -33,7 +33,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert {"fa_fwd", "fa_strerror", "fa_version"} <= set(declared_functions())
+    assert {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace", "fa_strerror",
+            "fa_version"} <= set(declared_functions())
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -48,7 +49,7 @@ def test_version(lib):
 def test_strerror_covers_every_code(lib):
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED_D,
              fa.FA_ERR_DTYPE, fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS,
-             fa.FA_ERR_HIP, fa.FA_ERR_ARG]
+             fa.FA_ERR_HIP, fa.FA_ERR_ARG, fa.FA_ERR_SPLITS, fa.FA_ERR_WORKSPACE]
     msgs = [fa.fa_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert fa.fa_strerror(12345) == "unknown status code"
@@ -113,3 +114,73 @@ def test_aliasing(lib, over):
 def test_fp32_shares_the_checks(lib):
     assert call(dtype=fa.FA_F32, d=96) == fa.FA_ERR_UNSUPPORTED_D
     assert call(dtype=fa.FA_F32, O=V) == fa.FA_ERR_ALIAS
+
+
+# ---- key-range split forward -------------------------------------------------
+
+def ws_bytes(B, H, N, d, S):
+    return S * B * H * N * (d + 1) * 4
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 64, 1), (2, 3, 100, 64, 4), (2, 32, 4096, 128, 8),
+                                   (1, 16, 16384, 128, 128)])
+def test_splitkv_workspace_size(lib, shape):
+    assert fa.fa_fwd_splitkv_workspace(*shape) == ws_bytes(*shape)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 1, 64, 1), fa.FA_ERR_SHAPE), ((1, 1, 0, 64, 1), fa.FA_ERR_SHAPE),
+    ((1, 1, 2**31, 64, 1), fa.FA_ERR_SHAPE), ((2**31, 2**31, 1, 64, 1), fa.FA_ERR_SHAPE),
+    ((1, 1, 8, 96, 1), fa.FA_ERR_UNSUPPORTED_D), ((1, 1, 8, 64, 0), fa.FA_ERR_SPLITS),
+    ((1, 1, 8, 64, 129), fa.FA_ERR_SPLITS), ((1, 1, 8, 64, -3), fa.FA_ERR_SPLITS)])
+def test_splitkv_workspace_errors(lib, args, code):
+    assert fa.fa_fwd_splitkv_workspace(*args) == code
+
+
+W = 11 * GB  # workspace; GOOD's shapes need 2*3*100*65*4*S bytes, far below 1 GB
+
+
+def call_split(S=4, ws=W, ws_bytes_=None, **over):
+    a = dict(GOOD, **over)
+    if ws_bytes_ is None:
+        ws_bytes_ = ws_bytes(a["B"], a["H"], a["N"], a["d"], S)
+    return fa.fa_fwd_splitkv(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["H"], a["N"],
+                             a["d"], a["scale"], a["causal"], a["stream"], a["dtype"], S, ws,
+                             ws_bytes_)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(L=None), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(dtype=5), fa.FA_ERR_DTYPE), (dict(scale=math.nan), fa.FA_ERR_SCALE),
+    (dict(causal=3), fa.FA_ERR_ARG), (dict(K=K + 4), fa.FA_ERR_ALIGN),
+    (dict(O=V), fa.FA_ERR_ALIAS)])
+def test_splitkv_shares_fwd_checks(lib, over, code):
+    assert call_split(**over) == code
+
+
+@pytest.mark.parametrize("S", [0, -1, 129, 1000])
+def test_splitkv_bad_splits(lib, S):
+    assert call_split(S=S, ws_bytes_=1 << 30) == fa.FA_ERR_SPLITS
+
+
+def test_splitkv_bad_workspace(lib):
+    need = ws_bytes(2, 3, 100, 64, 4)
+    assert call_split(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call_split(ws_bytes_=need - 1) == fa.FA_ERR_WORKSPACE
+    assert call_split(ws_bytes_=-1) == fa.FA_ERR_WORKSPACE
+    assert call_split(ws=W + 128) == fa.FA_ERR_WORKSPACE
+    assert call_split(ws=W + 4) == fa.FA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("ws", [Q, K + 256, V - 256, O, L - 1024])
+def test_splitkv_workspace_alias(lib, ws):
+    assert call_split(ws=ws) == fa.FA_ERR_ALIAS
+
+
+def test_splitkv_grid_too_large(lib):
+    # B*H*ceil(N/32)*S workgroups must fit a 32-bit grid.
+    T = 1 << 40  # addresses far enough apart for 2**30 rows
+    far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T)
+    assert call_split(S=128, ws=6 * T, B=1, H=1, N=2**30, ws_bytes_=2**62, **far) == \
+        fa.FA_ERR_SHAPE

@@ -57,7 +57,16 @@ STRESS = Workload("stress_bf16_b16h16n2048d64", 16, 16, 2048, 64, "bf16", False,
                   stress=True)
 
 ALL = (TINY_FP32, MULTIHEAD, CAUSAL_4K, LONG_16K, STRESS)
-BY_NAME = {w.name: w for w in ALL}
+
+# Key-range split workloads: few query tiles per head, so one workgroup per
+# 256-row query tile covers only part of the chip's 256 compute units.  Each
+# entry names the shape and the number of key ranges the split path uses.
+LOWOCC_8K = Workload("lowocc_bf16_b1h4n8192d128", 1, 4, 8192, 128, "bf16", False)
+LOWOCC_8K_CAUSAL = Workload("lowocc_causal_bf16_b1h8n8192d128", 1, 8, 8192, 128, "bf16", True)
+SPLIT = ((LOWOCC_8K, 4), (LOWOCC_8K_CAUSAL, 4))
+
+BY_NAME = {w.name: w for w in ALL + tuple(w for w, _ in SPLIT)}
+SPLITS_OF = {w.name: s for w, s in SPLIT}
 
 # The stress workload: Q and K drawn with standard deviation 3, and a per-row
 # offset c ~ U(-20, 20) added to every component of the *scaled* query, i.e.
