@@ -6,7 +6,8 @@
 
 One step is one fa_fwd call (the whole forward: QK^T, online softmax, PV,
 normalisation, O and L written) over one batch of seeded synthetic inputs
-already resident in device memory.  The default workload is the causal bf16
+already resident in device memory (200 untimed warm-up steps, then 100 timed
+steps, by default).  The default workload is the causal bf16
 case B=2, H=32, N=4096, d=128, on which the MFMA-peak target is stated.
 
 For the key-range split workloads (few query tiles per head) a step is one
@@ -114,8 +115,11 @@ def cpu_baseline(w, seed, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU's clocks take about 30 ms of back-to-back launches to settle
+    # (about 100 launches of the causal 4096 workload); 200 warm-up steps
+    # put every timed step in the steady state.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--splits", type=int, default=0,

@@ -52,15 +52,27 @@
 
 namespace fa355 {
 
-constexpr int kBM = 256;       // query rows per workgroup
-constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+#ifndef FA355_BF16_WAVES
+#define FA355_BF16_WAVES 8
+#endif
 #ifndef FA355_BF16_STAGES
 #define FA355_BF16_STAGES 3
 #endif
-constexpr int kStages = FA355_BF16_STAGES;  // ring depth of the K and V tile buffers
-static_assert(kStages >= 3, "the loop reads K two tiles ahead of V");
+#ifndef FA355_BF16_VSTAGES
+#define FA355_BF16_VSTAGES FA355_BF16_STAGES
+#endif
+constexpr int kWaves = FA355_BF16_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup (32 per wave)
+constexpr int kBN = 64;           // keys per K/V tile
+constexpr int kStages = FA355_BF16_STAGES;    // ring depth of the K tile buffers
+constexpr int kVStages = FA355_BF16_VSTAGES;  // ring depth of the V tile buffers
+// The loop reads K two tiles ahead of V.  Either both rings are kStages >= 3
+// deep, or K is 3 deep and V 2 deep (each V tile then loads during the one
+// iteration before it is read).
+static_assert((kStages >= 3 && kVStages == kStages) || (kStages == 3 && kVStages == 2),
+              "ring depths");
+static_assert(kWaves == 4 || kWaves == 8, "waves per workgroup");
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
 
 // LDS image of one tile (64 keys x D, bf16):
@@ -73,8 +85,8 @@ struct Bf16Layout {
   static constexpr int kKSlab = kBN * 32;             // 2 KB
   static constexpr int kVSlab = kBN * 64;             // 4 KB
   static constexpr int kOffK = 0;                     // kStages K tiles
-  static constexpr int kOffV = kStages * kTileBytes;  // kStages V tiles
-  static constexpr int kBytes = 2 * kStages * kTileBytes;  // 32 KB per stage at d = 128
+  static constexpr int kOffV = kStages * kTileBytes;  // kVStages V tiles
+  static constexpr int kBytes = (kStages + kVStages) * kTileBytes;  // 16 KB per slot at d = 128
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
   static constexpr int kLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
   static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
@@ -325,7 +337,8 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& 
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Lse, int N,
     int BH, int num_qtiles, float scale, float scale_log2, SplitArgs split_args) {
@@ -342,10 +355,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
 
   int bh, qt, split = 0;
   if (SPLIT && CAUSAL) {
-    // Longest first: query tiles from the last (most visible keys) down; in
-    // each, the key ranges from the first (whole) to the ones past the
-    // diagonal (empty); heads fastest, so that consecutive workgroups, which
-    // land on different XCDs, keep each head on one XCD.
+    // Longest first: query tiles from the last (most visible keys) down, all
+    // key ranges of a tile together (they have equal work); heads fastest, so
+    // that consecutive workgroups, which land on different XCDs, keep each
+    // head on one XCD.
     const int per_level = BH * split_args.num_splits;
     const int level = blockIdx.x / per_level;
     const int r = blockIdx.x - level * per_level;
@@ -371,9 +384,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
 
   // Keys of this workgroup: [kv_lo, kv_hi) (the whole row without SPLIT).
   // Tiles the workgroup streams, and the prefix of them this wave needs.
-  static_assert(kBM == kSplitRows && kBN == kSplitKeys, "split blocks are workgroup tiles");
+  static_assert(kSplitRows % kBM == 0 && kBN == kSplitKeys, "split blocks hold whole tiles");
   int kv_lo = 0, kv_hi = N;
-  if (SPLIT) split_range(split, split_args.num_splits, qt, N, CAUSAL, kv_lo, kv_hi);
+  if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
   const int kv_end = CAUSAL ? min(kv_hi, q0 + kBM) : kv_hi;
   const int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
   int my_tiles = 0;
@@ -543,10 +556,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
   // A workgroup whose key range is empty (a split past the causal diagonal)
   // skips straight to the epilogue, which then writes L = -inf and O = 0.
   if (n_tiles > 0) {
-    // Prologue.  Ring slots: tile j lives in slot j % kStages of its ring.
-    // Iteration t reads V_t and K_{t+2} and refills the slots of K_{t+1} and
-    // V_{t-1} (read in iteration t-1) with K_{t+1+S} and V_{t-1+S}, S =
-    // kStages.  Before iteration 0, K_0..K_2 and V_0 must have landed; the
+    // Prologue.  Ring slots: K tile j lives in slot j % kStages, V tile j in
+    // slot j % kVStages.  Iteration t reads V_t and K_{t+2}.  It refills the
+    // slot of K_{t+1} (read in iteration t-1) with K_{t+1+kStages}, and the
+    // V slot freed by iteration t-1 with V_{t-1+kVStages}.  Before iteration
+    // 0, K_0..K_2 and V_0 must have landed.  With equal ring depths S, the
     // loads of the "iterations" 2-S .. -1 are issued here in loop order so
     // that the vmcnt at the end of every iteration stays exact.  K_S goes to
     // the slot of K_0, which the prologue's scores read, so it waits for the
@@ -555,13 +569,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     load_k(1, 1);
     load_k(2, 2);
     load_v(0, 0);
-  #pragma unroll
-    for (int j = 3; j < kStages; ++j) {
-      load_k(j, j);
-      load_v(j - 2, j - 2);
+    if constexpr (kVStages == kStages) {
+#pragma unroll
+      for (int j = 3; j < kStages; ++j) {
+        load_k(j, j);
+        load_v(j - 2, j - 2);
+      }
+      load_v(kStages - 2, kStages - 2);
+      wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
+    } else {
+      wait_vmcnt<0>();  // a 2-deep V ring: iteration 0 loads V_1
     }
-    load_v(kStages - 2, kStages - 2);
-    wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
     block_sync();
 
     f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
@@ -577,65 +595,76 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(
     block_sync();  // every wave is done reading K_0 before its slot is refilled
     load_k(0, kStages);
 
-    // One tile.  Slot sv = t % S holds V_t; K_{t+2} is in slot (t+2) % S.  On
-    // entry pf holds P_t and cur the raw scores of tile t+1; nxt receives tile
-    // t+2.
+    // One tile.  On entry pf holds P_t and cur the raw scores of tile t+1;
+    // nxt receives tile t+2.  sk = t % kStages is the K ring position (K_{t+2}
+    // is in slot (sk+2) % kStages); svs = t % kVStages is V_t's slot.
     auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
-    // The loads of later tiles (K_{t+1+S} and V_{t-1+S}, into slots freed by
-    // the previous barrier) are issued inside the two MFMA phases rather than
-    // all at the top: eight waves issuing them at once right after the barrier
-    // queue up in the address unit.
-    auto iteration = [&](int t, int sv, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+    // The loads of later tiles are issued inside the two MFMA phases rather
+    // than all at the top: eight waves issuing them at once right after the
+    // barrier queue up in the address unit.  With a 2-deep V ring the V load
+    // goes first, so that it has the whole iteration to land.
+    constexpr bool kShortV = kVStages == 2;
+    auto refill_v = [&](int t, int sk, int svs) {
+      if constexpr (kShortV) load_v(svs ^ 1, t + 1);
+      else load_v(wrap(sk + kStages - 1), t - 1 + kStages);
+    };
+    auto iteration = [&](int t, int sk, int svs, f32x16(&cur)[2], f32x16(&nxt)[2]) {
       if (t + 1 < my_tiles) {
         mask_tile(t + 1, cur);
         // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
         // the K load of a later tile in the middle.
         SoftmaxState st;
-        pv_tile<D>(v_addr(sv), pf, oacc, [&](auto ic) {
+        pv_tile<D>(v_addr(svs), pf, oacc, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage1Steps>{},
                     [&](auto sic) { stage1_step(sic, cur, st); });
-          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sv + 1), t + 1 + kStages);
+          if constexpr (kShortV && decltype(ic)::value == 0) refill_v(t, sk, svs);
+          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sk + 1), t + 1 + kStages);
         });
         pin_scores(cur);
         asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
 
         // Phase 2: move the output to the new reference (rare).
         if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
         }
 
         // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
         // with the V load of a later tile in the middle.
-        score_tile<D>(k_addr(wrap(sv + 2)), qf, nxt, [&](auto ic) {
+        score_tile<D>(k_addr(wrap(sk + 2)), qf, nxt, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage2Steps>{},
                     [&](auto sic) { stage2_step(sic, cur, st, pf); });
-          if constexpr (decltype(ic)::value == kMf / 2)
-            load_v(wrap(sv + kStages - 1), t - 1 + kStages);
+          if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(t, sk, svs);
         });
         pin_probs(pf);
       } else {
-        load_k(wrap(sv + 1), t + 1 + kStages);
-        if (t < my_tiles) pv_tile<D>(v_addr(sv), pf, oacc);
-        load_v(wrap(sv + kStages - 1), t - 1 + kStages);
+        if constexpr (kShortV) refill_v(t, sk, svs);
+        load_k(wrap(sk + 1), t + 1 + kStages);
+        if (t < my_tiles) pv_tile<D>(v_addr(svs), pf, oacc);
+        if constexpr (!kShortV) refill_v(t, sk, svs);
       }
 
-      // K_{t+3} and V_{t+1} (issued in iteration t+2-S) must have landed for
-      // every wave before anyone reads them; the loads of the S-2 later
-      // iterations may stay in flight.
-      wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
+      // K_{t+3} and V_{t+1} must have landed for every wave before anyone
+      // reads them.  Equal rings: both were issued in iteration t+2-S, and the
+      // loads of the S-2 later iterations may stay in flight.  2-deep V ring:
+      // V_{t+1} was this iteration's first load; only its K load may stay.
+      if constexpr (kShortV) wait_vmcnt<kVmPerTile>();
+      else wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
       block_sync();
     };
 
     // Two tiles per trip so that the two score buffers swap roles instead of
-    // being copied.
-    int t = 0, sv = 0;
+    // being copied (and, with a 2-deep V ring, V slots are constants).
+    int t = 0, sk = 0;
     for (; t + 1 < n_tiles; t += 2) {
-      iteration(t, sv, sB, sA);
-      iteration(t + 1, wrap(sv + 1), sA, sB);
-      sv = wrap(sv + 2);
+      iteration(t, sk, kShortV ? 0 : sk, sB, sA);
+      iteration(t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
+      sk = wrap(sk + 2);
     }
-    if (t < n_tiles) iteration(t, sv, sB, sA);
+    if (t < n_tiles) iteration(t, sk, kShortV ? 0 : sk, sB, sA);
+    // The ring's last refills (clamped repeats of the last tile) are still in
+    // flight; let them land before the workgroup can end and its LDS be reused.
+    wait_vmcnt<0>();
   }
 
   // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
