@@ -54,6 +54,9 @@ int check_args(const void* Q, const void* K, const void* V, void* O, float* L, i
   const uint64_t rows = (uint64_t)BH * (uint64_t)N;
   if (rows > (UINT64_MAX / 4) / ((uint64_t)d * esize)) return FA_ERR_SHAPE;
   const uint64_t tensor_bytes = rows * (uint64_t)d * esize;
+  // The bf16 kernel reads K and V through buffer resources whose size field
+  // holds one head (N * d * 2 bytes) as a 32-bit signed count.
+  if (dtype == FA_BF16 && (uint64_t)N * (uint64_t)d * 2 > (uint64_t)INT_MAX) return FA_ERR_SHAPE;
   const uint64_t lse_bytes = rows * 4;
 
   const uintptr_t misalign = reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) |

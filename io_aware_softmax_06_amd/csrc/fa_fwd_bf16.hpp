@@ -166,43 +166,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Direct global->LDS copy of one K or V tile.  Each wave issues kLoadsPerWave
-// instructions; lane l of instruction (slice) i fills bytes [16l, 16l+16) of
-// the tile's i-th kilobyte and fetches the 16 bytes of K or V that the layout
-// puts there.  Rows past N are clamped to row N-1: their scores are masked and
-// their probabilities are 0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile_part(char* smem, int buf_off,
-                                               const uint16_t* __restrict__ src_head, int kv0,
-                                               int N, int wave, int lane, int r) {
-  using Lay = Bf16Layout<D>;
-  {
-    const int slice = wave * Lay::kLoadsPerWave + r;
-    int row, col;
-    if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
-      row = 16 * (slice & 3) + (lane >> 2);
-      col = 32 * (slice >> 2) + 8 * (lane & 3);
-    } else {     // slab s = slice / 2 holds rows 32 (slice % 2) .. +31
-      row = 32 * (slice & 1) + (lane >> 1);
-      col = 16 * (slice >> 1) + 8 * ((lane & 1) ^ ((row >> 3) & 1));
-    }
-    const int key = min(kv0 + row, N - 1);
-    const uint16_t* src = src_head + (size_t)key * D + col;
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<__attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(src)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(
-            reinterpret_cast<uintptr_t>(smem + buf_off + slice * 1024)),
-        16, 0, 0);
-  }
+// Direct global->LDS copy of one K or V tile through a buffer resource.
+// Each wave issues kLoadsPerWave buffer_load_dwordx4 ... lds instructions;
+// lane l of instruction (slice) i fills bytes [16l, 16l+16) of the tile's
+// i-th kilobyte and fetches the 16 bytes of K or V that the layout puts
+// there.  One resource per head covers exactly its N rows and is built once;
+// the per-lane byte offset is a loop constant plus the tile's offset, and the
+// hardware range check on that offset returns zeros for rows past N (their
+// scores are masked and their probabilities are 0), so no row is clamped.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_resource(const uint16_t* head, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(head), (short)0, bytes,
+                                           kBufferWord3);
 }
 
 template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane, int r) {
+  using Lay = Bf16Layout<D>;
+  const int slice = wave * Lay::kLoadsPerWave + r;
+  int row, col;
+  if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
+    row = 16 * (slice & 3) + (lane >> 2);
+    col = 32 * (slice >> 2) + 8 * (lane & 3);
+  } else {     // slab s = slice / 2 holds rows 32 (slice % 2) .. +31
+    row = 32 * (slice & 1) + (lane >> 1);
+    col = 16 * (slice >> 1) + 8 * ((lane & 1) ^ ((row >> 3) & 1));
+  }
+  return (uint32_t)(row * D + col) * 2u;
+}
+
+// rsrc: the head's K or V (head_resource); kv0: first row of the tile; the
+// lane offsets come from tile_lane_offset.
+template <int D>
 __device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
-                                                 const uint16_t* __restrict__ src_head, int kv0,
-                                                 int N, int wave, int lane) {
+                                                 __amdgpu_buffer_rsrc_t rsrc, int kv0, int wave,
+                                                 const uint32_t* lane_off) {
+  using Lay = Bf16Layout<D>;
+  const uint32_t tile_off = (uint32_t)kv0 * (D * 2);
 #pragma unroll
-  for (int r = 0; r < Bf16Layout<D>::kLoadsPerWave; ++r)
-    load_tile_part<D, IS_V>(smem, buf_off, src_head, kv0, N, wave, lane, r);
+  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
+    const int slice = wave * Lay::kLoadsPerWave + r;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc,
+        reinterpret_cast<__attribute__((address_space(3))) void*>(
+            reinterpret_cast<uintptr_t>(smem + buf_off + slice * 1024)),
+        16, lane_off[r] + tile_off, 0, 0, 0);
+  }
 }
 
 // Scores of one tile, transposed: sacc[kb] = K[32kb + key_of_row(.)] Q^T.
@@ -425,13 +435,22 @@ fa_fwd_bf16_kernel(
   const uint32_t smem_lds = lds_address(smem);
   auto k_addr = [&](int slot) { return smem_lds + Lay::kOffK + slot * Lay::kTileBytes + k_lane; };
   auto v_addr = [&](int slot) { return smem_lds + Lay::kOffV + slot * Lay::kTileBytes + v_lane; };
+  uint32_t k_off[kVmPerTile], v_off[kVmPerTile];
+#pragma unroll
+  for (int r = 0; r < kVmPerTile; ++r) {
+    k_off[r] = tile_lane_offset<D, false>(wave, lane, r);
+    v_off[r] = tile_lane_offset<D, true>(wave, lane, r);
+  }
+  const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(Kb, N * D * 2);
+  const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(Vb, N * D * 2);
+  // Tiles past the last one (the ring's final refills) reload the last tile.
   auto load_k = [&](int slot, int tile) {
-    load_tile_direct<D, false>(smem, Lay::kOffK + slot * Lay::kTileBytes, Kb,
-                               kv_lo + min(tile, last) * kBN, N, wave, lane);
+    load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes, k_rsrc,
+                        kv_lo + min(tile, last) * kBN, wave, k_off);
   };
   auto load_v = [&](int slot, int tile) {
-    load_tile_direct<D, true>(smem, Lay::kOffV + slot * Lay::kTileBytes, Vb,
-                              kv_lo + min(tile, last) * kBN, N, wave, lane);
+    load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes, v_rsrc,
+                        kv_lo + min(tile, last) * kBN, wave, v_off);
   };
 
   // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
@@ -455,13 +474,15 @@ fa_fwd_bf16_kernel(
   };
   // The softmax of a tile as numbered steps, so that each MFMA of a phase can
   // be given its share (step s of NS goes after MFMA s * kMf / NS).
-  // Stage 1 (18 steps): the eight partial maxima, the row maximum and the
-  // reference update, eight pairs of exponentials of block 0, their sum.
+  // Stage 1 (18 steps): the row maximum as a chain of three-input maxima
+  // (two per step), the half-wave exchange and reference update, eight pairs
+  // of exponentials of block 0, their sum.
   // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
-  // into l_run, eight pairs of bf16 conversions into the P^T operands.
+  // into l_run, eight pairs of bf16 conversions into the P^T operands.  The
+  // sums are taken over the float32 probabilities: summing their bf16
+  // roundings instead would move L by up to 2^-9 on rows with few keys.
   struct SoftmaxState {
-    float m8[8];
-    float alpha, half_sum;
+    float m, alpha, half_sum;
     bool need;
   };
   constexpr int kStage1Steps = 18, kStage2Steps = 17;
@@ -469,11 +490,11 @@ fa_fwd_bf16_kernel(
     constexpr int sidx = decltype(sic)::value;
     if constexpr (sidx < 8) {
       constexpr int kb = sidx >> 2, e = 4 * (sidx & 3);
-      st.m8[sidx] = fmaxf(fmaxf(sc[kb][e], sc[kb][e + 1]), fmaxf(sc[kb][e + 2], sc[kb][e + 3]));
+      if constexpr (sidx == 0) st.m = fmaxf(sc[0][0], sc[0][1]);
+      else st.m = fmaxf(fmaxf(st.m, sc[kb][e]), sc[kb][e + 1]);
+      st.m = fmaxf(fmaxf(st.m, sc[kb][e + 2]), sc[kb][e + 3]);
     } else if constexpr (sidx == 8) {
-      float mx = fmaxf(fmaxf(fmaxf(st.m8[0], st.m8[1]), fmaxf(st.m8[2], st.m8[3])),
-                       fmaxf(fmaxf(st.m8[4], st.m8[5]), fmaxf(st.m8[6], st.m8[7])));
-      mx = max_halves(mx);
+      const float mx = max_halves(st.m);
       const float cand = mx * scale_log2;  // -inf for a fully masked tile
       st.need = cand > base_run + kTau;
       const float base_new = st.need ? cand : base_run;
