@@ -79,6 +79,15 @@ def test_bad_shape(lib, over):
     assert call(**over) == fa.FA_ERR_SHAPE
 
 
+def test_bf16_head_must_fit_32bit_offsets(lib):
+    # N * d * 2 >= 2^31 is rejected for bf16 only; addresses far apart so that
+    # only the size check can decide.
+    T = 1 << 44
+    far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T, B=1, H=1)
+    assert call(N=2**23, d=128, **far) == fa.FA_ERR_SHAPE
+    assert call(N=2**24, d=64, **far) == fa.FA_ERR_SHAPE
+
+
 @pytest.mark.parametrize("d", [0, 1, 32, 63, 65, 96, 127, 129, 256])
 def test_unsupported_head_dim(lib, d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED_D
