@@ -28,7 +28,9 @@ Modules:
                 its natural-log logsumexp L (materialised S, fp64); a per-row
                 form for sampled checks at full size; the tiled one-pass online
                 algorithm in the pages' order (used only to show that it
-                reaches the definition).
+                reaches the definition); the partial result over a key range
+                and the merge of partials; the definition under a block mask
+                (block-sparse attention, [P3] introduction).
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against
 something other than itself (closed forms, brute force with ``math.fsum``,
@@ -51,4 +53,6 @@ from .exact_attention import (  # noqa: F401
     attention_online_tiled,
     attention_partial,
     merge_partials,
+    attention_block_sparse,
+    expand_block_mask,
 )

@@ -66,6 +66,61 @@ def attention(q, k, v, scale, causal=False):
     return O, L
 
 
+def expand_block_mask(block_mask, n_q, block=64, n_k=None):
+    """Boolean [n_q, n_k] element mask (True = visible) of a block mask.
+
+    Query i and key j are in blocks i // block and j // block; the last block
+    of each side may be partial.  n_k defaults to n_q.
+    """
+    n_k = n_q if n_k is None else n_k
+    bm = np.asarray(block_mask) != 0
+    return bm[np.ix_(np.arange(n_q) // block, np.arange(n_k) // block)]
+
+
+def attention_block_sparse(q, k, v, scale, causal, block_mask, block=64):
+    """The definition with a block mask: key j is visible to query i iff the
+    block (i // block, j // block) is set (and, with ``causal``, j <= i).
+
+    The Triton article's introduction ([P3]) extends the tiled kernel to
+    block-sparse attention without stating it further; this is the plainest
+    reading: hidden scores are -inf before the softmax, exactly as the causal
+    mask, so a row with no visible key is O = 0, L = -inf.  ``block_mask`` is
+    [nbq, nbk] (shared by every head), [H, nbq, nbk] (per head) or
+    [B, H, nbq, nbk], with nbq = ceil(N_q / block), nbk = ceil(N_k / block).
+    Returns (O, L) in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    bm = np.asarray(block_mask)
+    nbq, nbk = -(-Nq // block), -(-Nk // block)
+    if bm.shape[-2:] != (nbq, nbk):
+        raise ValueError(f"block mask must end in ({nbq}, {nbk})")
+    if bm.ndim == 2:
+        bm = np.broadcast_to(bm, (B, H, nbq, nbk))
+    elif bm.ndim == 3:
+        bm = np.broadcast_to(bm[None], (B, H, nbq, nbk))
+    O = np.zeros((B, H, Nq, v.shape[-1]))
+    L = np.zeros((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ k[b, h].T)
+            hidden = ~expand_block_mask(bm[b, h], Nq, block, Nk)
+            if causal:
+                hidden |= _causal_mask(Nq, 0, Nk)
+            S[hidden] = -np.inf
+            m = S.max(axis=1)
+            dead = ~np.isfinite(m)
+            m_safe = np.where(dead, 0.0, m)
+            E = np.exp(S - m_safe[:, None])
+            l = E.sum(axis=1)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                P = np.where(dead[:, None], 0.0, E / np.where(dead, 1.0, l)[:, None])
+                O[b, h] = P @ v[b, h]
+                L[b, h] = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, l)))
+    return O, L
+
+
 def attention_rows(q, k, v, scale, causal, rows):
     """The definition for selected query rows only.
 

@@ -199,8 +199,18 @@ def _by_partials(q, k, v, scale, causal):
     return oatt.merge_partials(parts)
 
 
+def _block_sparse_all_ones(block):
+    def att(q, k, v, scale, causal):
+        nbq, nbk = -(-q.shape[2] // block), -(-k.shape[2] // block)
+        return oracle.attention_block_sparse(q, k, v, scale, causal,
+                                             np.ones((nbq, nbk), np.uint8), block)
+    return att
+
+
 IMPLEMENTATIONS = {
     "definition": oracle.attention,
+    "block_sparse_all_ones_b4": _block_sparse_all_ones(4),
+    "block_sparse_all_ones_b64": _block_sparse_all_ones(64),
     "tiled_4x4": _tiled(4, 4),
     "tiled_3x5": _tiled(3, 5),
     "tiled_16x7": _tiled(16, 7),
@@ -517,3 +527,168 @@ def _states_subtracted_factor(x):
 def test_worked_example_catches_wrong_rescale(states_fn):
     with pytest.raises(AssertionError):
         check_worked_example(states_fn)
+
+
+# ----------------------------------------------------------------------------
+# block-sparse pins: the mask itself
+
+
+def brute_attention_masked(q, k, v, scale, visible):
+    """Scalar loops with math.exp / math.fsum; visible(b, h, i, j) -> bool."""
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, v.shape[-1]))
+    L = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                vis = [j for j in range(N) if visible(b, h, i, j)]
+                if not vis:
+                    L[b, h, i] = -math.inf
+                    continue
+                s = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t])
+                                       for t in range(d)) for j in vis]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                tot = math.fsum(e)
+                for t in range(v.shape[-1]):
+                    O[b, h, i, t] = math.fsum(e[n] * float(v[b, h, j, t])
+                                              for n, j in enumerate(vis)) / tot
+                L[b, h, i] = m + math.log(tot)
+    return O, L
+
+
+def check_block_mask_brute_force(att_bs):
+    """Random masks (per head), tiny blocks, ragged N, with and without causal."""
+    rng = np.random.default_rng(21)
+    for N, block in ((5, 2), (8, 3), (13, 4)):
+        nb = -(-N // block)
+        B, H, d = 1, 2, 3
+        q, k, v = (_rand(rng, B, H, N, d) for _ in range(3))
+        bm = (rng.random((H, nb, nb)) < 0.5).astype(np.uint8)
+        bm[0, 0, :] = 0  # an empty block row: its queries see nothing
+        for causal in (False, True):
+            O, L = att_bs(q, k, v, 0.6, causal, bm, block)
+
+            def visible(b, h, i, j):
+                return bool(bm[h, i // block, j // block]) and (not causal or j <= i)
+            Ob, Lb = brute_attention_masked(q, k, v, 0.6, visible)
+            np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-13)
+            assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
+            fin = np.isfinite(Lb)
+            np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-13)
+            assert np.all(O[np.isneginf(Lb)] == 0)
+
+
+def check_block_mask_closed_forms(att_bs):
+    rng = np.random.default_rng(22)
+    B, H, N, d, block = 2, 3, 12, 4, 4
+    q, k, v = (_rand(rng, B, H, N, d) for _ in range(3))
+    nb = N // block
+    # block-diagonal: every block of queries attends to its own block of keys only
+    O, L = att_bs(q, k, v, 0.5, False, np.eye(nb, dtype=np.uint8), block)
+    for r in range(nb):
+        sl = slice(r * block, (r + 1) * block)
+        Or, Lr = oracle.attention(q[:, :, sl], k[:, :, sl], v[:, :, sl], 0.5, False)
+        np.testing.assert_allclose(O[:, :, sl], Or, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, sl], Lr, atol=1e-14)
+    # an all-zero mask: nothing is visible anywhere
+    O, L = att_bs(q, k, v, 0.5, True, np.zeros((nb, nb), np.uint8), block)
+    assert np.all(O == 0) and np.all(np.isneginf(L))
+    # lower block-triangle with causal equals plain causal attention
+    O, L = att_bs(q, k, v, 0.5, True, np.tril(np.ones((nb, nb), np.uint8)), block)
+    Oc, Lc = oracle.attention(q, k, v, 0.5, True)
+    np.testing.assert_allclose(O, Oc, atol=1e-14)
+    np.testing.assert_allclose(L, Lc, atol=1e-14)
+
+
+def check_block_mask_invariants(att_bs):
+    rng = np.random.default_rng(23)
+    B, H, N, d, block = 2, 2, 10, 3, 3
+    nb = -(-N // block)
+    q, k, v = (_rand(rng, B, H, N, d) for _ in range(3))
+    bm = (rng.random((B, H, nb, nb)) < 0.6).astype(np.uint8)
+    O, L = att_bs(q, k, v, 0.4, False, bm, block)
+    # keys and values that no query sees do not matter
+    seen = oracle.expand_block_mask(bm[0, 0], N, block).any(axis=0)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, ~seen] += 100.0
+    v2[0, 0, ~seen] -= 7.0
+    O2, L2 = att_bs(q, k2, v2, 0.4, False, bm, block)
+    np.testing.assert_allclose(O2[0, 0], O[0, 0], atol=1e-14)
+    np.testing.assert_allclose(L2[0, 0], L[0, 0], atol=1e-14)
+    # a mask shared by all heads equals the same mask given per head
+    shared = bm[1, 0]
+    Os, Ls = att_bs(q, k, v, 0.4, True, shared, block)
+    Op, Lp = att_bs(q, k, v, 0.4, True, np.broadcast_to(shared, (B, H, nb, nb)).copy(), block)
+    np.testing.assert_array_equal(Os, Op)
+    np.testing.assert_array_equal(Ls, Lp)
+
+
+BLOCK_MASK_PINS = (check_block_mask_brute_force, check_block_mask_closed_forms,
+                   check_block_mask_invariants)
+
+
+@pytest.mark.parametrize("pin", BLOCK_MASK_PINS, ids=lambda f: f.__name__)
+def test_block_mask_pins(pin):
+    pin(oracle.attention_block_sparse)
+
+
+def test_expand_block_mask_ragged():
+    bm = np.array([[1, 0], [0, 1]], np.uint8)
+    e = oracle.expand_block_mask(bm, 5, 3)
+    want = np.zeros((5, 5), bool)
+    want[:3, :3] = True
+    want[3:, 3:] = True
+    np.testing.assert_array_equal(e, want)
+
+
+def _mutant_mask_transposed(q, k, v, scale, causal, bm, block):
+    # reads the block mask as [key block, query block]
+    bm = np.asarray(bm)
+    return oracle.attention_block_sparse(q, k, v, scale, causal, np.swapaxes(bm, -1, -2), block)
+
+
+def _mutant_mask_ignored(q, k, v, scale, causal, bm, block):
+    nb = np.asarray(bm).shape[-1]
+    return oracle.attention_block_sparse(q, k, v, scale, causal, np.ones((nb, nb), np.uint8),
+                                         block)
+
+
+def _mutant_mask_shifted_block(q, k, v, scale, causal, bm, block):
+    # block of an index taken as (index + 1) // block (an off-by-one)
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, H, N, d = q.shape
+    bm = np.asarray(bm)
+    nb = bm.shape[-1]
+    full = np.broadcast_to(bm if bm.ndim == 4 else bm[None] if bm.ndim == 3 else bm[None, None],
+                           (B, H, nb, nb))
+    O = np.zeros((B, H, N, d))
+    L = np.zeros((B, H, N))
+    idx = np.minimum((np.arange(N) + 1) // block, nb - 1)
+    for b in range(B):
+        for h in range(H):
+            vis = full[b, h][np.ix_(idx, idx)] != 0
+            if causal:
+                vis &= np.arange(N)[None, :] <= np.arange(N)[:, None]
+            S = np.where(vis, scale * (q[b, h] @ k[b, h].T), -np.inf)
+            m = S.max(1)
+            dead = ~np.isfinite(m)
+            ms = np.where(dead, 0.0, m)
+            E = np.exp(S - ms[:, None])
+            l = E.sum(1)
+            O[b, h] = np.where(dead[:, None], 0.0, (E / np.where(dead, 1.0, l)[:, None]) @ v[b, h])
+            L[b, h] = np.where(dead, -np.inf, ms + np.log(np.where(dead, 1.0, l)))
+    return O, L
+
+
+@pytest.mark.parametrize("mutant", [_mutant_mask_transposed, _mutant_mask_ignored,
+                                    _mutant_mask_shifted_block], ids=lambda f: f.__name__)
+def test_block_mask_pins_catch_planted_mistakes(mutant):
+    caught = []
+    for pin in BLOCK_MASK_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mutant)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "no block-mask pin caught the planted mistake"
