@@ -10,6 +10,11 @@ already resident in device memory (200 untimed warm-up steps, then 100 timed
 steps, by default).  The default workload is the causal bf16
 case B=2, H=32, N=4096, d=128, on which the MFMA-peak target is stated.
 
+For the block-sparse workload a step is one fa_fwd_blocksparse call with its
+local-global block mask (64 x 64 blocks); `value` then counts 4*d flops per
+visible (query, key) pair of the mask, and the line also carries fa_fwd on the
+same inputs (all pairs) under `dense`.
+
 For the key-range split workloads (few query tiles per head) a step is one
 fa_fwd_splitkv call instead: the split kernel and the merge kernel, with the
 workspace allocated before the timed region.  The line then also carries the
@@ -47,6 +52,17 @@ def attention_flops(w):
     return f / 2.0 if w.causal else f
 
 
+def visible_pairs(mask, N, causal, block=64):
+    """(query, key) pairs a [nb, nb] block mask (shared by all heads) leaves
+    visible: the flop count of the block-sparse workload is 4 d per pair."""
+    import torch
+    idx = torch.arange(N) // block
+    vis = mask.cpu().bool()[idx][:, idx]
+    if causal:
+        vis &= torch.ones((N, N), dtype=torch.bool).tril()
+    return int(vis.sum())
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
@@ -78,8 +94,11 @@ def measured_traffic(workload_name):
         return None
 
 
-def cpu_baseline(w, seed, budget_s=10.0):
-    """The float64 oracle on whole heads of the same inputs, ~budget_s seconds."""
+def cpu_baseline(w, seed, budget_s=10.0, block_mask=None, flops=None):
+    """The float64 oracle on whole heads of the same inputs, ~budget_s seconds.
+
+    With a block mask (shared by all heads) the oracle is the block-sparse
+    definition and ``flops`` the workload's count of useful flops."""
     import numpy as np
     import oracle
     from workloads import make_inputs, to_f64_numpy
@@ -94,13 +113,17 @@ def cpu_baseline(w, seed, budget_s=10.0):
     t0 = time.perf_counter()
     for (b, h) in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.attention(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]), to_f64_numpy(v[sl]),
-                         w.scale, w.causal)
+        if block_mask is None:
+            oracle.attention(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]), to_f64_numpy(v[sl]),
+                             w.scale, w.causal)
+        else:
+            oracle.attention_block_sparse(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]),
+                                          to_f64_numpy(v[sl]), w.scale, w.causal, block_mask)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    per_head = attention_flops(w) / (w.B * w.H)
+    per_head = (flops if flops is not None else attention_flops(w)) / (w.B * w.H)
     del np
     return {
         "value": round(per_head * done / dt / 1e12, 6),
@@ -148,6 +171,12 @@ def main():
     O = torch.empty_like(q)
     L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    sparse_mask = None
+    flops = attention_flops(w)
+    if w.name == workloads.SPARSE_4K.name:
+        sparse_mask = workloads.local_global_block_mask(
+            (w.N + 63) // 64, workloads.SPARSE_4K_WINDOW, workloads.SPARSE_4K_GLOBAL).to(dev)
+        flops = 4.0 * w.d * w.B * w.H * visible_pairs(sparse_mask, w.N, w.causal)
     splits = args.splits or workloads.SPLITS_OF.get(w.name, 0)
     ws = None
     if splits:
@@ -163,7 +192,11 @@ def main():
         fa.fwd_splitkv(q, k, v, splits, scale=w.scale, causal=w.causal, out=O, lse=L,
                        workspace=ws, stream=stream)
 
-    step = split_step if splits else unsplit_step
+    def sparse_step():
+        fa.fwd_blocksparse(q, k, v, sparse_mask, scale=w.scale, causal=w.causal, out=O, lse=L,
+                           stream=stream)
+
+    step = sparse_step if sparse_mask is not None else split_step if splits else unsplit_step
 
     def timed(fn, n):
         """(wall seconds, per-step event milliseconds) of n calls on `stream`."""
@@ -186,6 +219,17 @@ def main():
     wall, launch_ms = timed(step, args.steps)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
+    dense = None
+    if sparse_mask is not None:  # after the timed region: every pair, on the same inputs
+        for _ in range(max(1, args.warmup // 2)):
+            unsplit_step()
+        _, ms = timed(unsplit_step, args.steps)
+        avg = sum(ms) / len(ms) / 1e3
+        dense = {"kernel_us": round(avg * 1e6, 2),
+                 "tflops_all_pairs": round(attention_flops(w) / avg / 1e12, 3),
+                 "sparse_speedup": round(avg / avg_launch_s, 3),
+                 "mask_density": round(flops / attention_flops(w), 4)}
+
     unsplit = None
     if splits:  # after the timed region: the single-pass kernel on the same inputs
         for _ in range(max(1, args.warmup // 2)):
@@ -205,7 +249,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    flops = attention_flops(w)
     ms_per_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_launch_s / 1e12
@@ -232,7 +275,12 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "layout": "[B,H,N,d]",
                    "parallelism": "single GPU",
-                   "entry_point": "fa_fwd_splitkv" if splits else "fa_fwd",
+                   "entry_point": ("fa_fwd_blocksparse" if sparse_mask is not None
+                                   else "fa_fwd_splitkv" if splits else "fa_fwd"),
+                   **({"block_mask": f"local-global, band {workloads.SPARSE_4K_WINDOW}, "
+                                     f"{workloads.SPARSE_4K_GLOBAL} global blocks, 64x64; "
+                                     "flops over visible pairs"}
+                      if sparse_mask is not None else {}),
                    **({"num_splits": splits} if splits else {})},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
@@ -247,9 +295,12 @@ def main():
         },
         "cpu_baseline": None,
         **({"unsplit": unsplit} if splits else {}),
+        **({"dense": dense} if sparse_mask is not None else {}),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.seed)
+        result["cpu_baseline"] = cpu_baseline(
+            w, args.seed, block_mask=None if sparse_mask is None else sparse_mask.cpu().numpy(),
+            flops=flops)
     print(json.dumps(result), flush=True)
 
 

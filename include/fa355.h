@@ -134,6 +134,36 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    float scale, int causal, void* stream, int dtype,
                    int num_splits, void* workspace, int64_t workspace_bytes);
 
+/*
+ * fa_fwd_blocksparse -- fa_fwd restricted to the key blocks a block mask
+ * enables (the block-sparse attention kernel announced in the introduction
+ * of the Triton article "理解 Flash Attention：在 Triton 中从头编写算法").
+ *
+ *   block_mask  device pointer, uint8 [mask_heads][nb][nb], nb = ceil(N/64),
+ *               row-major, owned by the caller, read only.  Byte [m][i][j]
+ *               nonzero: the queries of 64-row block i may see the keys of
+ *               64-key block j (the last block of each side may be partial).
+ *   mask_heads  1 (one mask for every head), H (mask h for head h of every
+ *               batch) or B*H (mask b*H + h).
+ *
+ * Key j is visible to query i iff block_mask[m][i/64][j/64] != 0 and, with
+ * causal = 1, j <= i.  Hidden scores are -inf before the softmax, so the
+ * result is the definition under that mask; a row with no visible key gets
+ * O = 0 and L = -inf.  Only key blocks that some query block of a
+ * workgroup sees are loaded and multiplied.  The other arguments, the
+ * ownership and the semantics are fa_fwd's.
+ *
+ * Errors: fa_fwd's checks, plus FA_ERR_NULL for a NULL mask, FA_ERR_ARG for
+ * another mask_heads, FA_ERR_ALIAS if the mask overlaps O or L, and
+ * FA_ERR_SHAPE when the per-workgroup list of key blocks (4 bytes per key
+ * block, held on chip next to the K and V buffers) does not fit: with bf16,
+ * N up to about 1,048,000 at d = 128.
+ */
+int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L,
+                       int64_t B, int64_t H, int64_t N, int64_t d,
+                       float scale, int causal, void* stream, int dtype,
+                       const uint8_t* block_mask, int64_t mask_heads);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -10,6 +10,8 @@ Raw C-ABI functions (same names and argument order as include/fa355.h):
     fa_fwd_splitkv_workspace(B, H, N, d, num_splits) -> int (bytes or status)
     fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype,
                    num_splits, workspace, workspace_bytes) -> int
+    fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype,
+                       block_mask, mask_heads) -> int
     fa_strerror(status) -> str
     fa_version() -> int
 where Q, K, V, O, L and stream are integer addresses.
@@ -18,6 +20,8 @@ Tensor front end:
     fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (O, L)
     fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, out=None,
                 lse=None, workspace=None) -> (O, L, workspace)
+    fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None,
+                    lse=None) -> (O, L)
 """
 
 import ctypes
@@ -74,6 +78,9 @@ def load(path=LIB_PATH):
                                    ctypes.c_float, ctypes.c_int, vp, ctypes.c_int,
                                    ctypes.c_int, vp, i64]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                       ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, i64]
+    lib.fa_fwd_blocksparse.restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -97,6 +104,13 @@ def fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_
     """Direct call of the C entry point; returns its status code."""
     return load().fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, float(scale), int(causal), stream,
                                  dtype, int(num_splits), workspace, workspace_bytes)
+
+
+def fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, block_mask,
+                       mask_heads):
+    """Direct call of the C entry point; returns its status code."""
+    return load().fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, float(scale), int(causal),
+                                     stream, dtype, block_mask, int(mask_heads))
 
 
 def fa_strerror(status):
@@ -196,3 +210,36 @@ def split_partials(workspace, num_splits, B, H, N, d):
     o = f[: num_splits * rows * d].view(num_splits, B, H, N, d)
     l = f[num_splits * rows * d:].view(num_splits, B, H, N)
     return o, l
+
+
+MASK_BLOCK = 64
+
+
+def fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None,
+                    stream=None):
+    """Block-sparse attention forward; returns (O, L).
+
+    ``block_mask`` is a uint8 device tensor [nb, nb], [H, nb, nb] or
+    [B, H, nb, nb] with nb = ceil(N / 64): entry [i, j] nonzero lets the
+    queries of 64-row block i see the keys of 64-key block j.
+    """
+    import torch
+    (B, H, N, d), scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    m = block_mask
+    if m.dtype != torch.uint8 or m.device != q.device or not m.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 tensor on q's device")
+    if m.dim() == 2 and m.shape == (nb, nb):
+        mask_heads = 1
+    elif m.dim() == 3 and m.shape == (H, nb, nb):
+        mask_heads = H
+    elif m.dim() == 4 and m.shape == (B, H, nb, nb):
+        mask_heads = B * H
+    else:
+        raise ValueError(f"block_mask must be [{nb}, {nb}], [H, {nb}, {nb}] or [B, H, {nb}, {nb}]")
+    rc = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                            stream.cuda_stream, _dtype_code(q), m.data_ptr(), mask_heads)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse

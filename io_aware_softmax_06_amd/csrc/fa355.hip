@@ -17,8 +17,9 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: key-range split forward and merge
+constexpr int kVersion = 300;  // 0.3.0: block-sparse forward
 constexpr int kMaxSplits = 128;
+constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -82,59 +83,73 @@ uint64_t split_workspace_bytes(uint64_t rows, int64_t d, int splits) {
 
 // The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
 // instance's limit once per process (device-independent attribute).
-template <int D, bool CAUSAL, bool SPLIT>
+// Dynamic LDS of a bf16 launch: the K and V rings, plus on the block-sparse
+// path the tile list (one word per key block) and one count per wave.
+template <int D, int MODE>
+int64_t bf16_lds_bytes(int64_t N) {
+  int64_t bytes = fa355::Bf16Layout<D>::kBytes;
+  if (MODE == fa355::kSparse) bytes += 4 * ((N + fa355::kMaskBlock - 1) / fa355::kMaskBlock + fa355::kWaves);
+  return bytes;
+}
+
+// The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
+// instance's limit once per process (device-independent attribute) to what
+// its largest launch may use.
+template <int D, bool CAUSAL, int MODE>
 hipError_t prepare_bf16() {
   static const hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::Bf16Layout<D>::kBytes);
+      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      MODE == fa355::kSparse ? kMaxLds : fa355::Bf16Layout<D>::kBytes);
   return status;
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
-                       int64_t BH, int64_t N, float scale, fa355::SplitArgs sa,
+                       int64_t BH, int64_t N, float scale, fa355::ModeArgs sa,
                        hipStream_t stream) {
-  const hipError_t prep = prepare_bf16<D, CAUSAL, SPLIT>();
+  const hipError_t prep = prepare_bf16<D, CAUSAL, MODE>();
   if (prep != hipSuccess) return prep;
   const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
-  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(total),
-                     dim3(fa355::kThreads), fa355::Bf16Layout<D>::kBytes, stream,
+  const unsigned lds = (unsigned)bf16_lds_bytes<D, MODE>(N);
+  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE>), dim3(total),
+                     dim3(fa355::kThreads), lds, stream,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), L, (int)N,
                      (int)BH, num_qtiles, scale, scale * fa355::kLog2e, sa);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
-                      int64_t N, float scale, fa355::SplitArgs sa, hipStream_t stream) {
+                      int64_t N, float scale, fa355::ModeArgs sa, hipStream_t stream) {
   constexpr int kRows = 64 / (D / 64);
   const int num_qtiles = (int)((N + kRows - 1) / kRows);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
-  hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, SPLIT>), dim3(total), dim3(64), 0,
+  hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, MODE>), dim3(total), dim3(64), 0,
                      stream, static_cast<const float*>(Q), static_cast<const float*>(K),
                      static_cast<const float*>(V), static_cast<float*>(O), L, (int)N, (int)BH,
                      num_qtiles, scale, scale * fa355::kLog2e, sa);
   return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <int MODE>
 hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, float* L,
                           int64_t BH, int64_t N, int64_t d, float scale, int causal, int dtype,
-                          fa355::SplitArgs sa, hipStream_t s) {
+                          fa355::ModeArgs sa, hipStream_t s) {
   if (dtype == FA_BF16) {
     if (d == 64)
-      return causal ? launch_bf16<64, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
-                    : launch_bf16<64, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
-    return causal ? launch_bf16<128, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
-                  : launch_bf16<128, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+      return causal ? launch_bf16<64, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                    : launch_bf16<64, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
+    return causal ? launch_bf16<128, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_bf16<128, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
   }
   if (d == 64)
-    return causal ? launch_f32<64, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
-                  : launch_f32<64, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
-  return causal ? launch_f32<128, true, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s)
-                : launch_f32<128, false, SPLIT>(Q, K, V, O, L, BH, N, scale, sa, s);
+    return causal ? launch_f32<64, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_f32<64, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
+  return causal ? launch_f32<128, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                : launch_f32<128, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
 }
 
 template <int D, typename OutT>
@@ -160,9 +175,9 @@ extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, floa
   if (rc != FA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
-  const fa355::SplitArgs whole = {1, nullptr, nullptr};
+  const fa355::ModeArgs whole = {1, nullptr, nullptr, nullptr, 1, (int)H};
   const hipError_t err =
-      launch_forward<false>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, whole, s);
+      launch_forward<fa355::kDense>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, whole, s);
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -201,12 +216,12 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
 
   float* opart = static_cast<float*>(workspace);
   float* lpart = opart + sz.rows * (uint64_t)d * (uint64_t)num_splits;
-  const fa355::SplitArgs sa = {num_splits, opart, lpart};
+  const fa355::ModeArgs sa = {num_splits, opart, lpart, nullptr, 1, (int)H};
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   hipError_t err =
-      launch_forward<true>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, sa, s);
+      launch_forward<fa355::kSplit>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, sa, s);
   if (err == hipSuccess) {
     if (dtype == FA_BF16)
       err = d == 64 ? launch_merge<64, uint16_t>(opart, lpart, O, L, num_splits, sz.rows, s)
@@ -215,6 +230,32 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
       err = d == 64 ? launch_merge<64, float>(opart, lpart, O, L, num_splits, sz.rows, s)
                     : launch_merge<128, float>(opart, lpart, O, L, num_splits, sz.rows, s);
   }
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L,
+                                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                  int causal, void* stream, int dtype, const uint8_t* block_mask,
+                                  int64_t mask_heads) {
+  Sizes sz;
+  const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
+  if (rc != FA_OK) return rc;
+  if (!block_mask) return FA_ERR_NULL;
+  if (mask_heads != 1 && mask_heads != H && mask_heads != sz.BH) return FA_ERR_ARG;
+  const int64_t nb = (N + fa355::kMaskBlock - 1) / fa355::kMaskBlock;
+  // The tile list lives in LDS next to the K and V rings.
+  const int64_t lds = d == 64 ? bf16_lds_bytes<64, fa355::kSparse>(N)
+                              : bf16_lds_bytes<128, fa355::kSparse>(N);
+  if (dtype == FA_BF16 && lds > kMaxLds) return FA_ERR_SHAPE;
+  const uint64_t mask_bytes = (uint64_t)mask_heads * (uint64_t)nb * (uint64_t)nb;
+  if (ranges_overlap(block_mask, mask_bytes, O, sz.tensor_bytes) ||
+      ranges_overlap(block_mask, mask_bytes, L, sz.lse_bytes))
+    return FA_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const fa355::ModeArgs ma = {1, nullptr, nullptr, block_mask, (int)mask_heads, (int)H};
+  const hipError_t err =
+      launch_forward<fa355::kSparse>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, ma, s);
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -32,7 +32,7 @@ __device__ __forceinline__ float other_half(float v) {
 // into S ranges of T_rb / S tiles each (T_rb = visible keys / kSplitKeys,
 // rounded up): range s is tiles [s T_rb / S, (s+1) T_rb / S).  Cutting the
 // visible keys, not all N, gives every range of a causal block the same work.
-// With SPLIT a workgroup covers one (row block part, range) pair and writes,
+// In kSplit mode a workgroup covers one (row block part, range) pair and writes,
 // instead of O and L, that range's partial result: the output normalised by
 // the range's own denominator, O_s (float32, [S][BH][N][d]), and the range's
 // logsumexp L_s (float32, [S][BH][N]; -inf and O_s = 0 where no key of the
@@ -40,11 +40,34 @@ __device__ __forceinline__ float other_half(float v) {
 constexpr int kSplitRows = 256;
 constexpr int kSplitKeys = 64;
 
-struct SplitArgs {
-  int num_splits;  // S (1 without SPLIT)
-  float* opart;    // O_s, SPLIT only
-  float* lpart;    // L_s, SPLIT only
+// What a kernel instance does besides plain attention over all (or all
+// causal) keys.
+enum PathMode : int {
+  kDense = 0,   // every key (or every key j <= i)
+  kSplit = 1,   // one key range per workgroup, partial results (SplitArgs)
+  kSparse = 2,  // only the key blocks a block mask enables (below)
 };
+
+// Block-sparse attention: key j is visible to query i iff the byte
+// mask[hm][i / kMaskBlock][j / kMaskBlock] is nonzero (and j <= i with the
+// causal mask), hm = 0 for a mask shared by all heads, h for one mask per
+// head, b*H + h for one per (batch, head).  A row with no visible key gets
+// O = 0 and L = -inf.
+constexpr int kMaskBlock = 64;
+
+struct ModeArgs {
+  int num_splits;             // kSplit: S (1 otherwise)
+  float* opart;               // kSplit: O_s
+  float* lpart;               // kSplit: L_s
+  const uint8_t* mask;        // kSparse: [mask_heads][nb][nb], nb = ceil(N / 64)
+  int mask_heads;             // kSparse: 1, H or B*H
+  int H;                      // kSparse: heads per batch
+};
+
+// Index of the block mask of head bh (= b*H + h).
+__device__ __forceinline__ int mask_head(const ModeArgs& ma, int bh) {
+  return ma.mask_heads == 1 ? 0 : ma.mask_heads == ma.H ? bh % ma.H : bh;
+}
 
 // [lo, hi) of range s of row block rb.
 __device__ __forceinline__ void split_range(int s, int S, int rb, int N, bool causal, int& lo,

@@ -346,12 +346,21 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& 
   }
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+// 32-bit LDS read from inline asm (see lds_tr16), for the block-sparse tile list.
+__device__ __forceinline__ uint32_t lds_read32(uint32_t lds_addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(lds_addr));
+  return v;
+}
+
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Lse, int N,
-    int BH, int num_qtiles, float scale, float scale_log2, SplitArgs split_args) {
+    int BH, int num_qtiles, float scale, float scale_log2, ModeArgs split_args) {
+  constexpr bool SPLIT = MODE == kSplit;
+  constexpr bool SPARSE = MODE == kSparse;
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
@@ -380,6 +389,20 @@ fa_fwd_bf16_kernel(
     split = blockIdx.x - q * split_args.num_splits;
     bh = q / num_qtiles;
     qt = q - bh * num_qtiles;
+  } else if (SPARSE && !CAUSAL) {
+    // Query tiles outermost, first to last: how much a tile streams depends
+    // on the mask, and the first rows are the ones a sparse pattern most
+    // often makes global (seeing every key), so they start first.  Heads stay
+    // whole on one XCD as in map_tile.
+    constexpr int kXcds = 8;
+    if (BH % kXcds == 0) {
+      const int hp = BH / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+      qt = slot / hp;
+      bh = xcd * hp + slot % hp;
+    } else {
+      qt = blockIdx.x / BH;
+      bh = blockIdx.x % BH;
+    }
   } else {
     map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
   }
@@ -398,11 +421,54 @@ fa_fwd_bf16_kernel(
   int kv_lo = 0, kv_hi = N;
   if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
   const int kv_end = CAUSAL ? min(kv_hi, q0 + kBM) : kv_hi;
-  const int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
+  int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
   int my_tiles = 0;
   if (wq0 < N) {
     const int wave_end = CAUSAL ? min(kv_hi, wq0 + 32) : kv_hi;
     my_tiles = wave_end > kv_lo ? (wave_end - kv_lo + kBN - 1) / kBN : 0;
+  }
+
+  // Block-sparse: the tile list, built in LDS past the K and V rings.  It
+  // holds, in increasing order, the key blocks that at least one of this
+  // workgroup's 64-row query blocks may see, each as (key block | bits << 24)
+  // with bit r set when query block r of the workgroup sees it.
+  const uint32_t list_off = Lay::kBytes;
+  if constexpr (SPARSE) {
+    constexpr int kQBlocks = kBM / kMaskBlock;
+    static_assert(kBN == kMaskBlock && kBM % kMaskBlock == 0, "mask blocks are tiles");
+    uint32_t* list = reinterpret_cast<uint32_t*>(smem + list_off);
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    int* counts = reinterpret_cast<int*>(list + nb);
+    const int qb0 = q0 / kMaskBlock;
+    const int kb_end = CAUSAL ? min(nb, qb0 + kQBlocks) : nb;
+    const int qblocks = min(kQBlocks, nb - qb0);
+    const uint8_t* mrow =
+        split_args.mask + ((size_t)mask_head(split_args, bh) * nb + qb0) * (size_t)nb;
+    int total = 0;
+    for (int c = 0; c < kb_end; c += kThreads) {
+      const int kb = c + tid;
+      uint32_t bits = 0;
+      if (kb < kb_end) {
+        for (int r = 0; r < qblocks; ++r)
+          if ((!CAUSAL || kb <= qb0 + r) && mrow[(size_t)r * nb + kb] != 0) bits |= 1u << r;
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+      if (lane == 0) counts[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int before = total, all = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int cw = counts[w];
+        before += w < wave ? cw : 0;
+        all += cw;
+      }
+      if (bits != 0)
+        list[before + __builtin_popcountll(bal & ((1ull << lane) - 1))] = (uint32_t)kb | (bits << 24);
+      total += all;
+      __syncthreads();
+    }
+    n_tiles = total;
+    my_tiles = wq0 < N ? total : 0;
   }
   const int last = n_tiles - 1;
 
@@ -443,14 +509,32 @@ fa_fwd_bf16_kernel(
   }
   const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(Kb, N * D * 2);
   const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(Vb, N * D * 2);
-  // Tiles past the last one (the ring's final refills) reload the last tile.
-  auto load_k = [&](int slot, int tile) {
-    load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes, k_rsrc,
-                        kv_lo + min(tile, last) * kBN, wave, k_off);
+  // Tile t of the workgroup as an entry: its key block, plus (block-sparse
+  // path) which query blocks see it.  Dense and split paths: key block
+  // kv_lo / kBN + t; block-sparse: the t-th list entry, read from LDS with
+  // asm (callers wait with lds_wait<0> and pin the result).  Entries past the
+  // last tile repeat it: the ring's final refills reload the last tile.
+  auto entry = [&](int tile) -> uint32_t {
+    const int t = min(tile, last);
+    if constexpr (SPARSE) return lds_read32(smem_lds + list_off + 4 * t);
+    else return (uint32_t)(kv_lo / kBN + t);
   };
-  auto load_v = [&](int slot, int tile) {
-    load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes, v_rsrc,
-                        kv_lo + min(tile, last) * kBN, wave, v_off);
+  // Orders uses of an entry after the lds_wait, and moves it to a scalar
+  // register (it is the same in every lane).
+  auto pin_entry = [](uint32_t& e) {
+    asm volatile("" : "+v"(e));
+    e = __builtin_amdgcn_readfirstlane(e);
+  };
+  auto entry_kv0 = [](uint32_t e) { return (int)(SPARSE ? e & 0xFFFFFFu : e) * kBN; };
+  // Does this wave's 64-row query block see the tile at all?
+  auto entry_seen = [&](uint32_t e) { return !SPARSE || ((e >> (24 + (wave >> 1))) & 1u) != 0; };
+  auto load_k = [&](int slot, uint32_t e) {
+    load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes, k_rsrc, entry_kv0(e), wave,
+                        k_off);
+  };
+  auto load_v = [&](int slot, uint32_t e) {
+    load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes, v_rsrc, entry_kv0(e), wave,
+                        v_off);
   };
 
   // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
@@ -459,16 +543,17 @@ fa_fwd_bf16_kernel(
   // bf16 B operands of O^T += V^T P^T (16-key step s2 takes elements
   // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
   // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
-  auto mask_tile = [&](int j, f32x16(&sc)[2]) {
-    const int kv0 = kv_lo + j * kBN;
-    const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
+  auto mask_tile = [&](uint32_t ent, f32x16(&sc)[2]) {
+    const int kv0 = entry_kv0(ent);
+    const bool hidden = !entry_seen(ent);  // a key block this wave's query block does not see
+    const bool need_mask = hidden || (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
-          if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
+          if (hidden || key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
         }
     }
   };
@@ -586,17 +671,35 @@ fa_fwd_bf16_kernel(
     // that the vmcnt at the end of every iteration stays exact.  K_S goes to
     // the slot of K_0, which the prologue's scores read, so it waits for the
     // second barrier.
-    load_k(0, 0);
-    load_k(1, 1);
-    load_k(2, 2);
-    load_v(0, 0);
+    uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);
+    if constexpr (SPARSE) {
+      lds_wait<0>();
+      pin_entry(e0);
+      pin_entry(e1);
+      pin_entry(e2);
+    }
+    load_k(0, e0);
+    load_k(1, e1);
+    load_k(2, e2);
+    load_v(0, e0);
     if constexpr (kVStages == kStages) {
 #pragma unroll
       for (int j = 3; j < kStages; ++j) {
-        load_k(j, j);
-        load_v(j - 2, j - 2);
+        uint32_t ej = entry(j), ev = entry(j - 2);
+        if constexpr (SPARSE) {
+          lds_wait<0>();
+          pin_entry(ej);
+          pin_entry(ev);
+        }
+        load_k(j, ej);
+        load_v(j - 2, ev);
       }
-      load_v(kStages - 2, kStages - 2);
+      uint32_t ev = entry(kStages - 2);
+      if constexpr (SPARSE) {
+        lds_wait<0>();
+        pin_entry(ev);
+      }
+      load_v(kStages - 2, ev);
       wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
     } else {
       wait_vmcnt<0>();  // a 2-deep V ring: iteration 0 loads V_1
@@ -608,13 +711,18 @@ fa_fwd_bf16_kernel(
     if (my_tiles > 0) {
       score_tile<D>(k_addr(0), qf, sA);
       score_tile<D>(k_addr(1), qf, sB);
-      mask_tile(0, sA);
+      mask_tile(e0, sA);
       SoftmaxState st;
       stage1(sA, st);
       stage2(sA, st, pf);
     }
+    uint32_t es = entry(kStages);
+    if constexpr (SPARSE) {
+      lds_wait<0>();
+      pin_entry(es);
+    }
     block_sync();  // every wave is done reading K_0 before its slot is refilled
-    load_k(0, kStages);
+    load_k(0, es);
 
     // One tile.  On entry pf holds P_t and cur the raw scores of tile t+1;
     // nxt receives tile t+2.  sk = t % kStages is the K ring position (K_{t+2}
@@ -625,21 +733,33 @@ fa_fwd_bf16_kernel(
     // barrier queue up in the address unit.  With a 2-deep V ring the V load
     // goes first, so that it has the whole iteration to land.
     constexpr bool kShortV = kVStages == 2;
-    auto refill_v = [&](int t, int sk, int svs) {
-      if constexpr (kShortV) load_v(svs ^ 1, t + 1);
-      else load_v(wrap(sk + kStages - 1), t - 1 + kStages);
+    auto refill_v = [&](int sk, int svs, uint32_t ev) {
+      if constexpr (kShortV) load_v(svs ^ 1, ev);
+      else load_v(wrap(sk + kStages - 1), ev);
     };
     auto iteration = [&](int t, int sk, int svs, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+      // Entries of this iteration: tile t+1 (masked now), the K tile
+      // t+1+kStages and the V tile (t+1 or t-1+kStages) loaded now.  On the
+      // block-sparse path they are read here, before any operand read of the
+      // iteration is in flight.
+      uint32_t e_next = entry(t + 1), e_k = entry(t + 1 + kStages);
+      uint32_t e_v = kShortV ? e_next : entry(t - 1 + kStages);
+      if constexpr (SPARSE) {
+        lds_wait<0>();
+        pin_entry(e_next);
+        pin_entry(e_k);
+        pin_entry(e_v);
+      }
       if (t + 1 < my_tiles) {
-        mask_tile(t + 1, cur);
+        mask_tile(e_next, cur);
         // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
         // the K load of a later tile in the middle.
         SoftmaxState st;
         pv_tile<D>(v_addr(svs), pf, oacc, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage1Steps>{},
                     [&](auto sic) { stage1_step(sic, cur, st); });
-          if constexpr (kShortV && decltype(ic)::value == 0) refill_v(t, sk, svs);
-          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sk + 1), t + 1 + kStages);
+          if constexpr (kShortV && decltype(ic)::value == 0) refill_v(sk, svs, e_v);
+          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sk + 1), e_k);
         });
         pin_scores(cur);
         asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
@@ -655,14 +775,14 @@ fa_fwd_bf16_kernel(
         score_tile<D>(k_addr(wrap(sk + 2)), qf, nxt, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage2Steps>{},
                     [&](auto sic) { stage2_step(sic, cur, st, pf); });
-          if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(t, sk, svs);
+          if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(sk, svs, e_v);
         });
         pin_probs(pf);
       } else {
-        if constexpr (kShortV) refill_v(t, sk, svs);
-        load_k(wrap(sk + 1), t + 1 + kStages);
+        if constexpr (kShortV) refill_v(sk, svs, e_v);
+        load_k(wrap(sk + 1), e_k);
         if (t < my_tiles) pv_tile<D>(v_addr(svs), pf, oacc);
-        if constexpr (!kShortV) refill_v(t, sk, svs);
+        if constexpr (!kShortV) refill_v(sk, svs, e_v);
       }
 
       // K_{t+3} and V_{t+1} must have landed for every wave before anyone

@@ -5,8 +5,10 @@
 // row per lane (two lanes per row when d = 128, each holding 64 of the d
 // components), 32-key tiles of K and V staged in LDS and read as broadcasts.
 // This is the exact-precision variant; bf16 inputs take the MFMA kernel.
-// With SPLIT the workgroup covers the key range of one split and writes the
-// partial result described at SplitArgs (fa_common.hpp) instead of O, L.
+// In kSplit mode the workgroup covers the key range of one split and writes
+// the partial result described at ModeArgs (fa_common.hpp) instead of O, L;
+// in kSparse mode it skips the 64-key blocks its query block does not see
+// (the workgroup's rows lie in one 64-row block of the mask).
 #pragma once
 
 #include "fa_common.hpp"
@@ -15,12 +17,14 @@ namespace fa355 {
 
 constexpr int kF32Keys = 32;  // keys per staged tile
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ Lse, int N, int BH, int num_qtiles, float scale,
-    float scale_log2, SplitArgs split_args) {
+    float scale_log2, ModeArgs split_args) {
   static_assert(D == 64 || D == 128, "head dimension");
+  constexpr bool SPLIT = MODE == kSplit;
+  constexpr bool SPARSE = MODE == kSparse;
   constexpr int kLanesPerRow = D / 64;
   constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
   constexpr int kDl = 64;                   // components of d held per lane
@@ -60,7 +64,14 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
   int kv_lo = 0, kv_hi = N;
   if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
   const int kv_end = CAUSAL ? min(kv_hi, q0 + kRows) : kv_hi;
+  static_assert(kMaskBlock % kF32Keys == 0 && kMaskBlock % kRows == 0, "mask blocks");
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const uint8_t* mrow = nullptr;
+  if (SPARSE)
+    mrow = split_args.mask +
+           ((size_t)mask_head(split_args, bh) * nb + q0 / kMaskBlock) * (size_t)nb;
   for (int kv0 = kv_lo; kv0 < kv_end; kv0 += kF32Keys) {
+    if (SPARSE && mrow[kv0 / kMaskBlock] == 0) continue;  // same for the whole workgroup
     __syncthreads();
     for (int c = lane; c < kF32Keys * (D / 4); c += 64) {
       const int row = c / (D / 4), col = c % (D / 4);

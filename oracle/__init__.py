@@ -54,5 +54,6 @@ from .exact_attention import (  # noqa: F401
     attention_partial,
     merge_partials,
     attention_block_sparse,
+    attention_block_sparse_rows,
     expand_block_mask,
 )

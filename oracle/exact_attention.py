@@ -121,6 +121,34 @@ def attention_block_sparse(q, k, v, scale, causal, block_mask, block=64):
     return O, L
 
 
+def attention_block_sparse_rows(q, k, v, scale, causal, block_mask, rows, block=64):
+    """``attention_block_sparse`` for selected rows (b, h, i) only, O(N d) each.
+
+    ``block_mask`` as in ``attention_block_sparse``.  Returns (O_rows [R, d],
+    L_rows [R]) in float64; a row with no visible key gives O = 0, L = -inf.
+    """
+    bm = np.asarray(block_mask)
+    N = k.shape[2]
+    O = np.zeros((len(rows), v.shape[-1]))
+    L = np.zeros(len(rows))
+    for n, (b, h, i) in enumerate(rows):
+        m = bm if bm.ndim == 2 else bm[h] if bm.ndim == 3 else bm[b, h]
+        kk, vv = _f64(k[b, h]), _f64(v[b, h])
+        s = scale * (kk @ _f64(q[b, h, i]))
+        vis = m[i // block, np.arange(N) // block] != 0
+        if causal:
+            vis &= np.arange(N) <= i
+        if not vis.any():
+            L[n] = -np.inf
+            continue
+        s = np.where(vis, s, -np.inf)
+        mx = s.max()
+        e = np.exp(s - mx)
+        O[n] = (e @ vv) / e.sum()
+        L[n] = mx + np.log(e.sum())
+    return O, L
+
+
 def attention_rows(q, k, v, scale, causal, rows):
     """The definition for selected query rows only.
 

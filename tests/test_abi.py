@@ -193,3 +193,38 @@ def test_splitkv_grid_too_large(lib):
     far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T)
     assert call_split(S=128, ws=6 * T, B=1, H=1, N=2**30, ws_bytes_=2**62, **far) == \
         fa.FA_ERR_SHAPE
+
+
+# ---- block-sparse forward ---------------------------------------------------
+
+M = 13 * GB  # block mask address, far from the tensors
+
+
+def call_sparse(mask=M, mask_heads=1, **over):
+    a = dict(GOOD, **over)
+    return fa.fa_fwd_blocksparse(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["H"], a["N"],
+                                 a["d"], a["scale"], a["causal"], a["stream"], a["dtype"], mask,
+                                 mask_heads)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(dtype=9), fa.FA_ERR_DTYPE),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(causal=7), fa.FA_ERR_ARG),
+    (dict(V=V + 8), fa.FA_ERR_ALIGN), (dict(O=K), fa.FA_ERR_ALIAS)])
+def test_blocksparse_shares_fwd_checks(lib, over, code):
+    assert call_sparse(**over) == code
+
+
+def test_blocksparse_mask_checks(lib):
+    assert call_sparse(mask=None) == fa.FA_ERR_NULL
+    for mh in (0, 2, 5, 7, -1):  # GOOD has B = 2, H = 3: valid are 1, 3 and 6
+        assert call_sparse(mask_heads=mh) == fa.FA_ERR_ARG
+    assert call_sparse(mask=O) == fa.FA_ERR_ALIAS
+    assert call_sparse(mask=L - 2) == fa.FA_ERR_ALIAS
+
+
+def test_blocksparse_list_must_fit_on_chip(lib):
+    T = 1 << 44
+    far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T, B=1, H=1, d=128)
+    assert call_sparse(mask=6 * T, N=2**21, **far) == fa.FA_ERR_SHAPE

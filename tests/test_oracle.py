@@ -692,3 +692,22 @@ def test_block_mask_pins_catch_planted_mistakes(mutant):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, "no block-mask pin caught the planted mistake"
+
+
+def test_block_sparse_rows_match_full():
+    rng = np.random.default_rng(24)
+    B, H, N, d, block = 2, 3, 23, 4, 5
+    q, k, v = (_rand(rng, B, H, N, d) for _ in range(3))
+    nb = -(-N // block)
+    for bm in ((rng.random((nb, nb)) < 0.5).astype(np.uint8),
+               (rng.random((H, nb, nb)) < 0.5).astype(np.uint8),
+               (rng.random((B, H, nb, nb)) < 0.5).astype(np.uint8)):
+        bm[..., 1, :] = 0  # block row 1 sees nothing
+        for causal in (False, True):
+            O, L = oracle.attention_block_sparse(q, k, v, 0.7, causal, bm, block)
+            rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(N)]
+            o, l = oracle.attention_block_sparse_rows(q, k, v, 0.7, causal, bm, rows, block)
+            np.testing.assert_allclose(o.reshape(O.shape), O, atol=1e-14)
+            assert np.array_equal(np.isneginf(l.reshape(L.shape)), np.isneginf(L))
+            fin = np.isfinite(L)
+            np.testing.assert_allclose(l.reshape(L.shape)[fin], L[fin], atol=1e-13)

@@ -106,3 +106,36 @@ def make_qkv(B, H, N, d, dtype, seed, stress=False, scale=None, device="cpu"):
 def to_f64_numpy(t):
     """Exact float64 copy of a (CPU or device) tensor for the oracle."""
     return t.detach().to("cpu", torch.float32).double().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Block masks for block-sparse attention (64 x 64 blocks).  Inputs only: these
+# draw which blocks are on; they compute nothing of the method.
+
+def random_block_mask(nb, density, seed, heads=None, device="cpu"):
+    """uint8 [nb, nb] (or [heads, nb, nb]) with each block on with probability
+    ``density``, from a seeded CPU generator."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (nb, nb) if heads is None else (heads, nb, nb)
+    m = (torch.rand(shape, generator=g) < density).to(torch.uint8)
+    return m.to(device)
+
+
+def local_global_block_mask(nb, window, n_global, device="cpu"):
+    """uint8 [nb, nb]: block (i, j) on when |i - j| <= window (a band of
+    2 window + 1 blocks around the diagonal) or when i or j is one of the
+    first n_global blocks (global rows and columns), the sliding-window plus
+    global-token pattern of long-sequence sparse attention."""
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    on = ((i - j).abs() <= window) | (i < n_global) | (j < n_global)
+    return on.to(torch.uint8).to(device)
+
+
+# The block-sparse workload: B=2, H=32, N=4096, d=128 (the causal workload's
+# shape) with a local-global mask: a band of 3 blocks on each side of the
+# diagonal and 2 global blocks, 64 x 64 blocks.
+SPARSE_4K = Workload("blocksparse_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf16", False)
+SPARSE_4K_WINDOW, SPARSE_4K_GLOBAL = 3, 2
+BY_NAME[SPARSE_4K.name] = SPARSE_4K
