@@ -31,6 +31,9 @@ Modules:
                 reaches the definition); the partial result over a key range
                 and the merge of partials; the definition under a block mask
                 (block-sparse attention, [P3] introduction).
+  backward   -- the gradients dQ, dK, dV of <dO, O> by the chain rule through
+                the row softmax, with S and P materialised ([P3] core idea:
+                recompute the score matrix in the backward pass).
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against
 something other than itself (closed forms, brute force with ``math.fsum``,
@@ -57,3 +60,4 @@ from .exact_attention import (  # noqa: F401
     attention_block_sparse_rows,
     expand_block_mask,
 )
+from .backward import attention_backward  # noqa: F401

@@ -711,3 +711,136 @@ def test_block_sparse_rows_match_full():
             assert np.array_equal(np.isneginf(l.reshape(L.shape)), np.isneginf(L))
             fin = np.isfinite(L)
             np.testing.assert_allclose(l.reshape(L.shape)[fin], L[fin], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# backward pins
+
+
+def _phi(q, k, v, do, scale, causal):
+    O, _ = oracle.attention(q, k, v, scale, causal)
+    return float(np.sum(O * do))
+
+
+def check_backward_finite_differences(bwd):
+    """Central differences of <dO, O(Q, K, V)> through the pinned forward oracle."""
+    rng = np.random.default_rng(31)
+    for N, d, causal in ((4, 3, False), (5, 2, True), (3, 4, True)):
+        q, k, v, do = (_rand(rng, 1, 2, N, d) for _ in range(4))
+        scale = 0.8
+        dq, dk, dv = bwd(q, k, v, do, scale, causal)
+        h = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args = {"q": q, "k": k, "v": v}
+                fp = _phi(**{**args, name: xp}, do=do, scale=scale, causal=causal)
+                fm = _phi(**{**args, name: xm}, do=do, scale=scale, causal=causal)
+                assert abs((fp - fm) / (2 * h) - g[idx]) <= 1e-7, (name, idx)
+
+
+def check_backward_library(bwd):
+    """torch autograd through its CPU attention in float64."""
+    rng = np.random.default_rng(32)
+    B, H, N, d = 2, 2, 19, 8
+    q, k, v, do = (_rand(rng, B, H, N, d) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_() for a in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                               scale=scale)
+        out.backward(torch.from_numpy(do))
+        dq, dk, dv = bwd(q, k, v, do, scale, causal)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def check_backward_invariants(bwd):
+    rng = np.random.default_rng(33)
+    B, H, N, d = 1, 2, 15, 5
+    q, k, v, do = (_rand(rng, B, H, N, d) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv = bwd(q, k, v, do, 0.6, causal)
+        # rows of P sum to 1: the value gradients add up to the output gradients
+        np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+        # rows of dS sum to 0: the key gradients add up to zero
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+        # shifting every key by one vector leaves P, hence every gradient, unchanged
+        c = _rand(rng, 1, 1, 1, d)
+        dq2, dk2, dv2 = bwd(q, k + c, v, do, 0.6, causal)
+        np.testing.assert_allclose(dq2, dq, atol=1e-12)
+        np.testing.assert_allclose(dk2, dk, atol=1e-12)
+        np.testing.assert_allclose(dv2, dv, atol=1e-12)
+        # linear in dO
+        do2 = _rand(rng, B, H, N, d)
+        g1 = bwd(q, k, v, do2, 0.6, causal)
+        g2 = bwd(q, k, v, 2.0 * do - do2, 0.6, causal)
+        for a, b_, c_ in zip((dq, dk, dv), g1, g2):
+            np.testing.assert_allclose(c_, 2.0 * a - b_, atol=1e-12)
+
+
+BACKWARD_PINS = (check_backward_finite_differences, check_backward_library,
+                 check_backward_invariants)
+
+
+@pytest.mark.parametrize("pin", BACKWARD_PINS, ids=lambda f: f.__name__)
+def test_backward_pins(pin):
+    pin(oracle.attention_backward)
+
+
+def _mutant_bwd_no_d(q, k, v, do, scale, causal):
+    # drops the row term sum_k P_ik dP_ik of the softmax Jacobian
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    B, H, N, d = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                S[np.triu(np.ones((N, N), bool), 1)] = -np.inf
+            E = np.exp(S - S.max(1, keepdims=True))
+            P = E / E.sum(1, keepdims=True)
+            dv[b, h] = P.T @ do[b, h]
+            dS = P * (do[b, h] @ v[b, h].T)
+            dq[b, h] = scale * dS @ k[b, h]
+            dk[b, h] = scale * dS.T @ q[b, h]
+    return dq, dk, dv
+
+
+def _mutant_bwd_dk_transposed_operand(q, k, v, do, scale, causal):
+    # dK from dS instead of dS^T (a transposed operand)
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    B, H, N, d = q.shape
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                S[np.triu(np.ones((N, N), bool), 1)] = -np.inf
+            E = np.exp(S - S.max(1, keepdims=True))
+            P = E / E.sum(1, keepdims=True)
+            dP = do[b, h] @ v[b, h].T
+            dS = P * (dP - (P * dP).sum(1, keepdims=True))
+            dk[b, h] = scale * (dS @ q[b, h])
+    return dq, dk, dv
+
+
+def _mutant_bwd_no_scale(q, k, v, do, scale, causal):
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    return dq / scale, dk, dv
+
+
+@pytest.mark.parametrize("mutant", [_mutant_bwd_no_d, _mutant_bwd_dk_transposed_operand,
+                                    _mutant_bwd_no_scale], ids=lambda f: f.__name__)
+def test_backward_pins_catch_planted_mistakes(mutant):
+    caught = []
+    for pin in BACKWARD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mutant)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "no backward pin caught the planted mistake"
