@@ -15,6 +15,11 @@ local-global block mask (64 x 64 blocks); `value` then counts 4*d flops per
 visible (query, key) pair of the mask, and the line also carries fa_fwd on the
 same inputs (all pairs) under `dense`.
 
+For the backward workload a step is one fa_bwd call (the row sums D, then the
+dK/dV and dQ kernels) on the forward's O and L computed before the timed
+region; `value` counts the conventional 10*B*H*N^2*d flops (two and a half
+forward passes: the recomputed S and four products), halved for causal.
+
 For the key-range split workloads (few query tiles per head) a step is one
 fa_fwd_splitkv call instead: the split kernel and the merge kernel, with the
 workspace allocated before the timed region.  The line then also carries the
@@ -135,6 +140,36 @@ def cpu_baseline(w, seed, budget_s=10.0, block_mask=None, flops=None):
     }
 
 
+def cpu_baseline_backward(w, seed, budget_s=10.0):
+    """The float64 backward oracle on whole heads of the same inputs."""
+    import oracle
+    from workloads import make_grad, make_inputs, to_f64_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q, k, v = make_inputs(w, seed)
+    do = make_grad(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
+    done, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.attention_backward(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]),
+                                      to_f64_numpy(v[sl]), to_f64_numpy(do[sl]), w.scale, w.causal)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = 2.5 * attention_flops(w) / (w.B * w.H)
+    return {"value": round(per_head * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, seed {seed}, "
+                      f"float64 NumPy backward oracle with materialised S and P, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +212,14 @@ def main():
         sparse_mask = workloads.local_global_block_mask(
             (w.N + 63) // 64, workloads.SPARSE_4K_WINDOW, workloads.SPARSE_4K_GLOBAL).to(dev)
         flops = 4.0 * w.d * w.B * w.H * visible_pairs(sparse_mask, w.N, w.causal)
+    backward = w.name == workloads.BWD_CAUSAL_4K.name
+    if backward:
+        flops = 2.5 * attention_flops(w)
+        do = workloads.make_grad(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, device=dev)
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L, stream=stream)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        bwd_ws = torch.empty(fa.fa_bwd_workspace(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                             device=dev)
     splits = args.splits or workloads.SPLITS_OF.get(w.name, 0)
     ws = None
     if splits:
@@ -196,7 +239,12 @@ def main():
         fa.fwd_blocksparse(q, k, v, sparse_mask, scale=w.scale, causal=w.causal, out=O, lse=L,
                            stream=stream)
 
-    step = sparse_step if sparse_mask is not None else split_step if splits else unsplit_step
+    def backward_step():
+        fa.bwd(q, k, v, O, do, L, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+               workspace=bwd_ws, stream=stream)
+
+    step = (backward_step if backward else sparse_step if sparse_mask is not None
+            else split_step if splits else unsplit_step)
 
     def timed(fn, n):
         """(wall seconds, per-step event milliseconds) of n calls on `stream`."""
@@ -275,7 +323,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "layout": "[B,H,N,d]",
                    "parallelism": "single GPU",
-                   "entry_point": ("fa_fwd_blocksparse" if sparse_mask is not None
+                   "entry_point": ("fa_bwd" if backward else
+                                   "fa_fwd_blocksparse" if sparse_mask is not None
                                    else "fa_fwd_splitkv" if splits else "fa_fwd"),
                    **({"block_mask": f"local-global, band {workloads.SPARSE_4K_WINDOW}, "
                                      f"{workloads.SPARSE_4K_GLOBAL} global blocks, 64x64; "
@@ -292,12 +341,16 @@ def main():
             "traffic": measured_traffic(w.name),
             **({"kernels": "split forward + merge (one step, both launches)"}
                if splits else {}),
+            **({"kernels": "row sums D + dK/dV + dQ (one step, three launches)"}
+               if backward else {}),
         },
         "cpu_baseline": None,
         **({"unsplit": unsplit} if splits else {}),
         **({"dense": dense} if sparse_mask is not None else {}),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and backward:
+        result["cpu_baseline"] = cpu_baseline_backward(w, args.seed)
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(
             w, args.seed, block_mask=None if sparse_mask is None else sparse_mask.cpu().numpy(),
             flops=flops)

@@ -12,6 +12,9 @@ Raw C-ABI functions (same names and argument order as include/fa355.h):
                    num_splits, workspace, workspace_bytes) -> int
     fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype,
                        block_mask, mask_heads) -> int
+    fa_bwd_workspace(B, H, N, d) -> int (bytes or status)
+    fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, scale, causal, stream, dtype,
+           workspace, workspace_bytes) -> int
     fa_strerror(status) -> str
     fa_version() -> int
 where Q, K, V, O, L and stream are integer addresses.
@@ -22,6 +25,8 @@ Tensor front end:
                 lse=None, workspace=None) -> (O, L, workspace)
     fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None,
                     lse=None) -> (O, L)
+    bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+        workspace=None) -> (dQ, dK, dV)
 """
 
 import ctypes
@@ -81,6 +86,11 @@ def load(path=LIB_PATH):
     lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                        ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, i64]
     lib.fa_fwd_blocksparse.restype = ctypes.c_int
+    lib.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
+    lib.fa_bwd_workspace.restype = i64
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                           ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, i64]
+    lib.fa_bwd.restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -111,6 +121,18 @@ def fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, 
     """Direct call of the C entry point; returns its status code."""
     return load().fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, float(scale), int(causal),
                                      stream, dtype, block_mask, int(mask_heads))
+
+
+def fa_bwd_workspace(B, H, N, d):
+    """Workspace bytes of fa_bwd, or a negative status."""
+    return load().fa_bwd_workspace(B, H, N, d)
+
+
+def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, scale, causal, stream, dtype, workspace,
+           workspace_bytes):
+    """Direct call of the C entry point; returns its status code."""
+    return load().fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, float(scale), int(causal),
+                         stream, dtype, workspace, workspace_bytes)
 
 
 def fa_strerror(status):
@@ -243,3 +265,38 @@ def fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
+
+
+def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Attention backward; returns (dQ, dK, dV) with q's dtype and shape.
+
+    ``o`` and ``lse`` are the forward's outputs for the same q, k, v, scale
+    and mask; ``do`` is the gradient of the loss with respect to o.  The
+    workspace (uint8, at least ``fa_bwd_workspace(...)`` bytes) receives the
+    row sums D = rowsum(do * o); it is allocated here when None.
+    """
+    import torch
+    (B, H, N, d), scale, _, _, stream = _prepare(q, k, v, scale, o, lse, stream)
+    if do.shape != q.shape or do.dtype != q.dtype or do.device != q.device or not do.is_contiguous():
+        raise ValueError("do must be a contiguous tensor like q")
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_like(q)
+        elif g.shape != q.shape or g.dtype != q.dtype or g.device != q.device or not g.is_contiguous():
+            raise ValueError("dq, dk and dv must be contiguous tensors like q")
+        grads.append(g)
+    need = fa_bwd_workspace(B, H, N, d)
+    if need < 0:
+        raise FaError(need)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q),
+                workspace.data_ptr(), ws_bytes)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return tuple(grads)

@@ -14,10 +14,12 @@
 #include "fa_fwd_bf16.hpp"
 #include "fa_fwd_f32.hpp"
 #include "fa_merge.hpp"
+#include "fa_bwd_bf16.hpp"
+#include "fa_bwd_f32.hpp"
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0: block-sparse forward
+constexpr int kVersion = 400;  // 0.4.0: backward pass
 constexpr int kMaxSplits = 128;
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
@@ -256,6 +258,144 @@ extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, v
   const fa355::ModeArgs ma = {1, nullptr, nullptr, block_mask, (int)mask_heads, (int)H};
   const hipError_t err =
       launch_forward<fa355::kSparse>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, ma, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* Dv, void* dQ, void* dK, void* dV,
+                           int64_t BH, int64_t N, float scale, hipStream_t s) {
+  static const hipError_t attr_kv = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::BwdKvLayout<D>::kBytes);
+  static const hipError_t attr_q = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, fa355::BwdQLayout<D>::kBytes);
+  if (attr_kv != hipSuccess) return attr_kv;
+  if (attr_q != hipSuccess) return attr_q;
+  const float c = scale * fa355::kLog2e;
+  const auto* q = static_cast<const uint16_t*>(Q);
+  const auto* k = static_cast<const uint16_t*>(K);
+  const auto* v = static_cast<const uint16_t*>(V);
+  const auto* g = static_cast<const uint16_t*>(dO);
+  const int nk = (int)((N + fa355::kBwdKvKeys - 1) / fa355::kBwdKvKeys);
+  const unsigned lds_kv = fa355::BwdKvLayout<D>::kBytes, lds_q = fa355::BwdQLayout<D>::kBytes;
+  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * nk)),
+                     dim3(64 * fa355::kBwdKvWaves), lds_kv, s, q, k, v, g, L, Dv,
+                     static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), (int)N, (int)BH, scale,
+                     c);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nq = (int)((N + fa355::kBM - 1) / fa355::kBM);
+  hipLaunchKernelGGL((fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * nq)),
+                     dim3(fa355::kThreads), lds_q, s, q, k, v, g, L, Dv,
+                     static_cast<uint16_t*>(dQ), (int)N, (int)BH, nq, scale, c);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const void* dO,
+                          const float* L, const float* Dv, void* dQ, void* dK, void* dV,
+                          int64_t BH, int64_t N, float scale, hipStream_t s) {
+  constexpr int kRows = 64 / (D / 64);
+  const float c = scale * fa355::kLog2e;
+  const auto* q = static_cast<const float*>(Q);
+  const auto* k = static_cast<const float*>(K);
+  const auto* v = static_cast<const float*>(V);
+  const auto* g = static_cast<const float*>(dO);
+  const int nt = (int)((N + kRows - 1) / kRows);
+  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * nt)),
+                     dim3(64), 0, s, q, k, v, g, L, Dv, static_cast<float*>(dK),
+                     static_cast<float*>(dV), (int)N, nt, scale, c);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((fa355::fa_bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * nt)),
+                     dim3(64), 0, s, q, k, v, g, L, Dv, static_cast<float*>(dQ), (int)N, nt, scale,
+                     c);
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_bwd_dot(const void* O, const void* dO, float* Dv, uint64_t rows, hipStream_t s) {
+  constexpr int kRowsPer = fa355::kDotThreads / (D / 8);
+  uint64_t blocks = (rows + kRowsPer - 1) / kRowsPer;
+  if (blocks > (1u << 20)) blocks = 1u << 20;
+  hipLaunchKernelGGL((fa355::fa_bwd_dot_kernel<D, T>), dim3((unsigned)blocks),
+                     dim3(fa355::kDotThreads), 0, s, static_cast<const T*>(O),
+                     static_cast<const T*>(dO), Dv, (int64_t)rows);
+  return hipGetLastError();
+}
+
+extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
+    return FA_ERR_SHAPE;
+  if (B * H > INT_MAX) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  return B * H * N * 4;
+}
+
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* L, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
+                      int64_t N, int64_t d, float scale, int causal, void* stream, int dtype,
+                      void* workspace, int64_t workspace_bytes) {
+  if (!dO || !dQ || !dK || !dV) return FA_ERR_NULL;
+  // fa_fwd's checks with O and L as the "outputs": shapes, dtype, scale,
+  // causal, alignment of Q, K, V, O and L, and no overlap of O or L with
+  // Q, K, V.
+  Sizes sz;
+  const int rc = check_args(Q, K, V, const_cast<void*>(O), const_cast<float*>(L), B, H, N, d,
+                            scale, causal, dtype, &sz);
+  if (rc != FA_OK) return rc;
+  const uintptr_t misalign = reinterpret_cast<uintptr_t>(dO) | reinterpret_cast<uintptr_t>(dQ) |
+                             reinterpret_cast<uintptr_t>(dK) | reinterpret_cast<uintptr_t>(dV);
+  if ((misalign & 15u) != 0) return FA_ERR_ALIGN;
+  const uint64_t need = sz.rows * 4;
+  if (!workspace || workspace_bytes < 0 || (uint64_t)workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FA_ERR_WORKSPACE;
+  // Every written buffer (dQ, dK, dV, workspace) overlaps no other buffer.
+  const void* outs[4] = {dQ, dK, dV, workspace};
+  const uint64_t out_bytes[4] = {sz.tensor_bytes, sz.tensor_bytes, sz.tensor_bytes, need};
+  const void* ins[6] = {Q, K, V, O, dO, L};
+  const uint64_t in_bytes[6] = {sz.tensor_bytes, sz.tensor_bytes, sz.tensor_bytes,
+                                sz.tensor_bytes, sz.tensor_bytes, sz.lse_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (ranges_overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ALIAS;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  float* Dv = static_cast<float*>(workspace);
+  hipError_t err;
+  if (dtype == FA_BF16) {
+    err = d == 64 ? launch_bwd_dot<64, uint16_t>(O, dO, Dv, sz.rows, s)
+                  : launch_bwd_dot<128, uint16_t>(O, dO, Dv, sz.rows, s);
+    if (err == hipSuccess) {
+      if (d == 64)
+        err = causal ? launch_bwd_bf16<64, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                     : launch_bwd_bf16<64, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+      else
+        err = causal ? launch_bwd_bf16<128, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                     : launch_bwd_bf16<128, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+    }
+  } else {
+    err = d == 64 ? launch_bwd_dot<64, float>(O, dO, Dv, sz.rows, s)
+                  : launch_bwd_dot<128, float>(O, dO, Dv, sz.rows, s);
+    if (err == hipSuccess) {
+      if (d == 64)
+        err = causal ? launch_bwd_f32<64, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                     : launch_bwd_f32<64, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+      else
+        err = causal ? launch_bwd_f32<128, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                     : launch_bwd_f32<128, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+    }
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -1,0 +1,395 @@
+// Attention backward, bf16 in / bf16 out, fp32 accumulation, on gfx950 MFMA.
+//
+// The gradients of <dO, O> recompute the score matrix from Q, K and the
+// forward's logsumexp L instead of storing it (the Triton article's section
+// on the core idea, 核心思想).  With P = exp(scale S - L) (hidden scores 0):
+//     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// D_i equals sum_j P_ij dP_ij because O = P V; it is computed once per row
+// by fa_bwd_dot_kernel.
+//
+// Two kernels, so that no result is accumulated across workgroups (no
+// atomics; the output is deterministic):
+//  * fa_bwd_dkdv_bf16_kernel: a workgroup owns 128 keys (4 waves x 32) and
+//    streams the query tiles of its head; K and V sit in registers as the B
+//    operands of S = Q K^T and dP = dO V^T (one key per lane), and dV^T and
+//    dK^T accumulate from P and dS taken straight from those accumulators.
+//  * fa_bwd_dq_bf16_kernel: a workgroup owns 256 queries (8 waves x 32) and
+//    streams the key tiles, like the forward: S^T = K Q^T and dP^T = V dO^T
+//    with one query per lane, then dQ^T += K^T dS^T.
+// Both reuse the forward's operand reads (score_tile, pv_tile) and tile
+// layouts: a tile whose rows are the MFMA A operand is stored K-style, a
+// tile read transposed (K^T, Q^T, dO^T) V-style.  Tiles are double buffered
+// with one barrier per tile.
+#pragma once
+
+#include "fa_fwd_bf16.hpp"
+
+namespace fa355 {
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id in float32, one row per D/8 threads.
+constexpr int kDotThreads = 256;
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(kDotThreads) void fa_bwd_dot_kernel(const T* __restrict__ O,
+                                                                 const T* __restrict__ dO,
+                                                                 float* __restrict__ Dv,
+                                                                 int64_t rows) {
+  constexpr int kPer = D / 8;  // threads per row: 8 or 16, a power of two inside one wave
+  constexpr int kRowsPer = kDotThreads / kPer;
+  const int c = threadIdx.x % kPer;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPer;
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPer + threadIdx.x / kPer; row < rows;
+       row += stride) {
+    float o[8], g[8];
+    load8(O + row * D + 8 * c, o);
+    load8(dO + row * D + 8 * c, g);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(o[i], g[i], acc);
+#pragma unroll
+    for (int off = kPer / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (c == 0) Dv[row] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the two bf16 kernels.
+
+// bf16 B operand of a 32-row MFMA column: elements 16s + 8hh + (0..7) of row
+// `row` (a key of K or V, or a query of Q or dO), s = 0 .. D/16 - 1.
+template <int D>
+__device__ __forceinline__ void load_b_operand(const uint16_t* __restrict__ head, int row, int hh,
+                                               bf16x8 (&f)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    f[s] = __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(head + (size_t)row * D + 16 * s + 8 * hh));
+}
+
+// 16-key (or 16-query) step s2 of a 32x64 accumulator pair as a bf16 B operand.
+__device__ __forceinline__ void to_b_operand(const f32x16 (&x)[2], bf16x8 (&f)[kBN / 16]) {
+#pragma unroll
+  for (int s2 = 0; s2 < kBN / 16; ++s2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[s2][j] = (__bf16)x[s2 >> 1][8 * (s2 & 1) + j];
+}
+
+// Store a transposed accumulator (lane = row of the output, element 4g+r of
+// block db = column 32db + 8g + 4hh + r) times `mul` as bf16.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* __restrict__ out_row, const f32x16 (&acc)[D / 32],
+                                          float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __bf16 o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(acc[db][4 * g + r] * mul);
+      *reinterpret_cast<u32x2*>(out_row + 32 * db + 8 * g + 4 * hh) = __builtin_bit_cast(u32x2, o4);
+    }
+}
+
+// 64 floats (one per row of a tile) straight into LDS; rows past the end of
+// the resource read as 0.  Issued by one wave.
+__device__ __forceinline__ void load_row_floats(char* smem, int off, __amdgpu_buffer_rsrc_t rsrc,
+                                                int row0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc,
+      reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(smem + off)),
+      4, (uint32_t)(row0 + lane) * 4u, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch*head, 128 keys); 4 waves, 32 keys each.
+constexpr int kBwdKvWaves = 4;
+constexpr int kBwdKvKeys = 32 * kBwdKvWaves;
+
+template <int D>
+struct BwdKvLayout {
+  static constexpr int kTile = Bf16Layout<D>::kTileBytes;  // 64 rows x D bf16
+  static constexpr int kOffQk = 0, kOffDok = kTile, kOffQv = 2 * kTile, kOffDov = 3 * kTile;
+  static constexpr int kOffL = 4 * kTile, kOffD = 4 * kTile + 256;
+  static constexpr int kStage = 4 * kTile + 512;
+  static constexpr int kBytes = 2 * kStage;
+  static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                        const float* __restrict__ Lse, const float* __restrict__ Dv,
+                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH,
+                        float scale, float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  using Lay = BwdKvLayout<D>;
+  constexpr int W = kBwdKvWaves;
+  constexpr int kPer = Bf16Layout<D>::kLoadsPerTile / W;  // loads per wave per tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qi = lane & 31, hh = lane >> 5;
+
+  // Workgroup -> (head, key block).  Heads stay whole on one XCD; with the
+  // causal mask the first key blocks see the most queries, so they go first.
+  const int nk = (N + kBwdKvKeys - 1) / kBwdKvKeys;
+  int bh, kt;
+  {
+    constexpr int kXcds = 8;
+    const int bid = blockIdx.x;
+    if (BH % kXcds == 0) {
+      const int hp = BH / kXcds, xcd = bid % kXcds, slot = bid / kXcds;
+      if (CAUSAL) {
+        kt = slot / hp;
+        bh = xcd * hp + slot % hp;
+      } else {
+        bh = xcd * hp + slot / nk;
+        kt = slot % nk;
+      }
+    } else if (CAUSAL) {
+      kt = bid / BH;
+      bh = bid % BH;
+    } else {
+      bh = bid / nk;
+      kt = bid % nk;
+    }
+  }
+  const int k0 = kt * kBwdKvKeys;
+  const int kw0 = k0 + 32 * wave;  // first key of this wave
+  const int key = kw0 + qi;        // this lane's key
+  const size_t head = (size_t)bh * N * D;
+
+  // K^T and V^T as B operands (one key per lane), fixed for the workgroup.
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_b_operand<D>(K + head, min(key, N - 1), hh, kf);
+  load_b_operand<D>(V + head, min(key, N - 1), hh, vf);
+
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dkacc[i] = f32x16{};
+    dvacc[i] = f32x16{};
+  }
+
+  // Query tiles: with the causal mask only those that reach this workgroup's
+  // first key.
+  const int nq = (N + kBN - 1) / kBN;
+  const int t0 = CAUSAL ? k0 / kBN : 0;
+
+  const int arow = key_of_row(qi);
+  const int k_lane = arow * 32 + 16 * (hh ^ ((arow >> 3) & 1));
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_lane = (8 * (g16 >> 1) + (j16 >> 2)) * 64 + 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+  const uint32_t smem_lds = lds_address(smem);
+  uint32_t k_off[kPer], v_off[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    k_off[r] = tile_lane_offset<D, false, W>(wave, lane, r);
+    v_off[r] = tile_lane_offset<D, true, W>(wave, lane, r);
+  }
+  const __amdgpu_buffer_rsrc_t q_rsrc = head_resource(Q + head, N * D * 2);
+  const __amdgpu_buffer_rsrc_t do_rsrc = head_resource(dO + head, N * D * 2);
+  const __amdgpu_buffer_rsrc_t l_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Lse + (size_t)bh * N), (short)0, N * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Dv + (size_t)bh * N), (short)0, N * 4, kBufferWord3);
+
+  auto load_tile = [&](int t) {
+    const int st = (t & 1) * Lay::kStage, q0 = t * kBN;
+    load_tile_direct<D, W>(smem, st + Lay::kOffQk, q_rsrc, q0, wave, k_off);
+    load_tile_direct<D, W>(smem, st + Lay::kOffDok, do_rsrc, q0, wave, k_off);
+    load_tile_direct<D, W>(smem, st + Lay::kOffQv, q_rsrc, q0, wave, v_off);
+    load_tile_direct<D, W>(smem, st + Lay::kOffDov, do_rsrc, q0, wave, v_off);
+    if (wave == 0) {
+      load_row_floats(smem, st + Lay::kOffL, l_rsrc, q0, lane);
+      load_row_floats(smem, st + Lay::kOffD, d_rsrc, q0, lane);
+    }
+  };
+
+  if (t0 < nq) load_tile(t0);
+  for (int t = t0; t < nq; ++t) {
+    wait_vmcnt<0>();
+    block_sync();  // tile t has landed for every wave; tile t-1's stage is free
+    if (t + 1 < nq) load_tile(t + 1);
+    const int q0 = t * kBN;
+    // A wave whose keys all lie after the tile's last query has nothing to do.
+    if (kw0 >= N || (CAUSAL && q0 + kBN - 1 < kw0)) continue;
+    const uint32_t st = smem_lds + (t & 1) * Lay::kStage;
+
+    // S[q][key] and dP[q][key]: element 4g+r of block kb is query
+    // q0 + 32kb + key_of_row(8g + 4hh + r).
+    f32x16 sacc[2], dpacc[2];
+    score_tile<D>(st + Lay::kOffQk + k_lane, kf, sacc);
+    score_tile<D>(st + Lay::kOffDok + k_lane, vf, dpacc);
+
+    // P = exp(scale S - L), dS = P (dP - D); the four queries of a group g
+    // are consecutive, so their L and D come as one 16-byte read each.
+    const float* Lt = reinterpret_cast<const float*>(smem + (t & 1) * Lay::kStage + Lay::kOffL);
+    const float* Dt = reinterpret_cast<const float*>(smem + (t & 1) * Lay::kStage + Lay::kOffD);
+    const bool need_mask = (q0 + kBN > N) || (CAUSAL && kw0 + 31 > q0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qoff);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qoff);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          // -inf for a row that saw no key makes its probabilities 0.
+          const float nl = l4[r] == kNegInf ? kNegInf : -l4[r] * kLog2e;
+          float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
+          if (need_mask) {
+            const int q = q0 + qoff + r;
+            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+          }
+          sacc[kb][e] = p;
+          dpacc[kb][e] = p * (dpacc[kb][e] - d4[r]);
+        }
+      }
+    bf16x8 pf[kBN / 16], dsf[kBN / 16];
+    to_b_operand(sacc, pf);
+    to_b_operand(dpacc, dsf);
+
+    // dV^T += dO^T P and dK^T += Q^T dS (lane = key).
+    pv_tile<D>(st + Lay::kOffDov + v_lane, pf, dvacc);
+    pv_tile<D>(st + Lay::kOffQv + v_lane, dsf, dkacc);
+  }
+
+  if (key < N) {
+    store_rows<D>(dK + head + (size_t)key * D, dkacc, scale, hh);
+    store_rows<D>(dV + head + (size_t)key * D, dvacc, 1.f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (batch*head, 256 queries), 8 waves x 32 queries.
+template <int D>
+struct BwdQLayout {
+  static constexpr int kTile = Bf16Layout<D>::kTileBytes;
+  static constexpr int kOffKk = 0, kOffVk = kTile, kOffKv = 2 * kTile;
+  static constexpr int kStage = 3 * kTile;
+  static constexpr int kBytes = 2 * kStage;
+  static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                      const float* __restrict__ Lse, const float* __restrict__ Dv,
+                      uint16_t* __restrict__ dQ, int N, int BH, int num_qtiles, float scale,
+                      float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  using Lay = BwdQLayout<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qi = lane & 31, hh = lane >> 5;
+
+  int bh, qt;
+  map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
+  const int q0 = qt * kBM;
+  const int wq0 = q0 + 32 * wave;
+  const int qrow = wq0 + qi;
+  const size_t head = (size_t)bh * N * D;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  int my_tiles = 0;
+  if (wq0 < N) my_tiles = ((CAUSAL ? min(N, wq0 + 32) : N) + kBN - 1) / kBN;
+
+  // Q^T and dO^T as B operands (one query per lane); this row's L and D.
+  bf16x8 qf[D / 16], dof[D / 16];
+  const int qr = min(qrow, N - 1);
+  load_b_operand<D>(Q + head, qr, hh, qf);
+  load_b_operand<D>(dO + head, qr, hh, dof);
+  const float lq = Lse[(size_t)bh * N + qr];
+  const float nl = lq == kNegInf ? kNegInf : -lq * kLog2e;
+  const float dq_row = Dv[(size_t)bh * N + qr];
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
+
+  const int arow = key_of_row(qi);
+  const int k_lane = arow * 32 + 16 * (hh ^ ((arow >> 3) & 1));
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_lane = (8 * (g16 >> 1) + (j16 >> 2)) * 64 + 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+  const uint32_t smem_lds = lds_address(smem);
+  constexpr int kPer = Bf16Layout<D>::kLoadsPerWave;
+  uint32_t k_off[kPer], v_off[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    k_off[r] = tile_lane_offset<D, false>(wave, lane, r);
+    v_off[r] = tile_lane_offset<D, true>(wave, lane, r);
+  }
+  const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(K + head, N * D * 2);
+  const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(V + head, N * D * 2);
+
+  auto load_tile = [&](int j) {
+    const int st = (j & 1) * Lay::kStage, kv0 = j * kBN;
+    load_tile_direct<D>(smem, st + Lay::kOffKk, k_rsrc, kv0, wave, k_off);
+    load_tile_direct<D>(smem, st + Lay::kOffVk, v_rsrc, kv0, wave, k_off);
+    load_tile_direct<D>(smem, st + Lay::kOffKv, k_rsrc, kv0, wave, v_off);
+  };
+
+  if (n_tiles > 0) load_tile(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmcnt<0>();
+    block_sync();
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j >= my_tiles) continue;
+    const int kv0 = j * kBN;
+    const uint32_t st = smem_lds + (j & 1) * Lay::kStage;
+
+    // S^T[key][q] and dP^T[key][q]: element 4g+r of block kb is key
+    // kv0 + 32kb + key_of_row(8g + 4hh + r); lane = query.
+    f32x16 sacc[2], dpacc[2];
+    score_tile<D>(st + Lay::kOffKk + k_lane, qf, sacc);
+    score_tile<D>(st + Lay::kOffVk + k_lane, dof, dpacc);
+    const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
+        if (need_mask) {
+          const int kk = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
+          if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+        }
+        dpacc[kb][e] = p * (dpacc[kb][e] - dq_row);
+      }
+    bf16x8 dsf[kBN / 16];
+    to_b_operand(dpacc, dsf);
+    // dQ^T += K^T dS^T (K read transposed from its V-style copy).
+    pv_tile<D>(st + Lay::kOffKv + v_lane, dsf, dqacc);
+  }
+
+  if (qrow < N) store_rows<D>(dQ + head + (size_t)qrow * D, dqacc, scale, hh);
+}
+
+}  // namespace fa355

@@ -181,10 +181,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_resource(const uint16_t* 
                                            kBufferWord3);
 }
 
-template <int D, bool IS_V>
+template <int D, bool IS_V, int W = kWaves>
 __device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane, int r) {
   using Lay = Bf16Layout<D>;
-  const int slice = wave * Lay::kLoadsPerWave + r;
+  const int slice = wave * (Lay::kLoadsPerTile / W) + r;
   int row, col;
   if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
     row = 16 * (slice & 3) + (lane >> 2);
@@ -197,16 +197,18 @@ __device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane, int r) 
 }
 
 // rsrc: the head's K or V (head_resource); kv0: first row of the tile; the
-// lane offsets come from tile_lane_offset.
-template <int D>
+// lane offsets come from tile_lane_offset; W waves share the tile's loads.
+template <int D, int W = kWaves>
 __device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
                                                  __amdgpu_buffer_rsrc_t rsrc, int kv0, int wave,
                                                  const uint32_t* lane_off) {
   using Lay = Bf16Layout<D>;
+  constexpr int kPer = Lay::kLoadsPerTile / W;
+  static_assert(kPer >= 1 && Lay::kLoadsPerTile % W == 0, "tile split over waves");
   const uint32_t tile_off = (uint32_t)kv0 * (D * 2);
 #pragma unroll
-  for (int r = 0; r < Lay::kLoadsPerWave; ++r) {
-    const int slice = wave * Lay::kLoadsPerWave + r;
+  for (int r = 0; r < kPer; ++r) {
+    const int slice = wave * kPer + r;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc,
         reinterpret_cast<__attribute__((address_space(3))) void*>(

@@ -228,3 +228,53 @@ def test_blocksparse_list_must_fit_on_chip(lib):
     T = 1 << 44
     far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T, B=1, H=1, d=128)
     assert call_sparse(mask=6 * T, N=2**21, **far) == fa.FA_ERR_SHAPE
+
+
+# ---- backward ---------------------------------------------------------------
+
+GQ, GK, GV, WSB = 15 * GB, 17 * GB, 19 * GB, 21 * GB  # dQ, dK, dV, workspace
+DO = 23 * GB
+
+
+def call_bwd(ws=WSB, ws_bytes_=None, **over):
+    a = dict(dict(GOOD, dO=DO, dQ=GQ, dK=GK, dV=GV), **over)
+    if ws_bytes_ is None:
+        ws_bytes_ = a["B"] * a["H"] * a["N"] * 4
+    return fa.fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], a["dQ"], a["dK"], a["dV"],
+                     a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"],
+                     a["dtype"], ws, ws_bytes_)
+
+
+def test_bwd_workspace_size(lib):
+    assert fa.fa_bwd_workspace(2, 32, 4096, 128) == 2 * 32 * 4096 * 4
+    assert fa.fa_bwd_workspace(1, 1, 0, 64) == fa.FA_ERR_SHAPE
+    assert fa.fa_bwd_workspace(1, 1, 8, 96) == fa.FA_ERR_UNSUPPORTED_D
+
+
+@pytest.mark.parametrize("field", ["Q", "K", "V", "O", "L", "dO", "dQ", "dK", "dV"])
+def test_bwd_null(lib, field):
+    assert call_bwd(**{field: None}) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(dtype=3), fa.FA_ERR_DTYPE), (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(causal=2), fa.FA_ERR_ARG), (dict(dO=DO + 8), fa.FA_ERR_ALIGN),
+    (dict(dK=GK + 2), fa.FA_ERR_ALIGN), (dict(L=L + 1), fa.FA_ERR_ALIGN)])
+def test_bwd_checks(lib, over, code):
+    assert call_bwd(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(dQ=Q), dict(dK=V + 16), dict(dV=O), dict(dQ=DO),
+                                  dict(dK=L - 64), dict(dV=GQ), dict(dK=GV - 16)])
+def test_bwd_alias(lib, over):
+    assert call_bwd(**over) == fa.FA_ERR_ALIAS
+
+
+def test_bwd_workspace_checks(lib):
+    need = 2 * 3 * 100 * 4
+    assert call_bwd(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call_bwd(ws_bytes_=need - 4) == fa.FA_ERR_WORKSPACE
+    assert call_bwd(ws=WSB + 64) == fa.FA_ERR_WORKSPACE
+    assert call_bwd(ws=GK) == fa.FA_ERR_ALIAS
+    assert call_bwd(ws=DO + 256) == fa.FA_ERR_ALIAS

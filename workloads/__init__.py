@@ -139,3 +139,19 @@ def local_global_block_mask(nb, window, n_global, device="cpu"):
 SPARSE_4K = Workload("blocksparse_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf16", False)
 SPARSE_4K_WINDOW, SPARSE_4K_GLOBAL = 3, 2
 BY_NAME[SPARSE_4K.name] = SPARSE_4K
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: the output gradient dO is drawn like V (standard normal, then
+# rounded to the workload's dtype) from its own seeded generator.
+
+def make_grad(B, H, N, d, dtype, seed, device="cpu"):
+    """Seeded dO of shape [B, H, N, d]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 1_000_003)
+    return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(dtype).to(device)
+
+
+# The backward workload: the causal shape B=2, H=32, N=4096, d=128 in bf16.
+BWD_CAUSAL_4K = Workload("bwd_causal_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf16", True)
+BY_NAME[BWD_CAUSAL_4K.name] = BWD_CAUSAL_4K
