@@ -24,7 +24,11 @@ extern "C" {
 /* Element type of Q, K, V and O. */
 typedef enum {
   FA_BF16 = 0, /* bfloat16 inputs and output, float32 accumulation */
-  FA_F32 = 1   /* float32 inputs and output, float32 arithmetic */
+  FA_F32 = 1,  /* float32 inputs and output, float32 arithmetic */
+  FA_F16 = 2   /* IEEE half inputs and output, float32 accumulation; the
+                  exponentials are taken in float32, so the half-precision
+                  overflow of e^x past x = 11.09 that the FlashAttention blog
+                  post's "(Safe) Softmax" section warns of does not arise */
 } fa_dtype;
 
 /* Status codes.  Every negative code except FA_ERR_HIP is returned by the
@@ -33,8 +37,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,           /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,          /* B, H or N < 1, or a size too large to index
-                                 (bf16: one head of K, N * d * 2 bytes, must be
-                                 below 2^31) */
+                                 (bf16, fp16: one head of K, N * d * 2 bytes,
+                                 must be below 2^31) */
   FA_ERR_UNSUPPORTED_D = -3,  /* head dimension d is not 64 or 128 */
   FA_ERR_DTYPE = -4,          /* dtype is not an fa_dtype value */
   FA_ERR_SCALE = -5,          /* scale is not finite or not > 0 */
@@ -56,8 +60,9 @@ typedef enum {
  *            logsumexp of each row's scaled, masked scores:
  *            L[b,h,i] = ln sum_j exp(scale * q_i . k_j).  Required (not NULL).
  *   B, H, N  batch, heads, sequence length (queries = keys = N); each >= 1.
- *            With FA_BF16, N * d * 2 must be below 2^31 (N < 8388608 at
- *            d = 128): K and V are read through 32-bit buffer offsets.
+ *            With FA_BF16 or FA_F16, N * d * 2 must be below 2^31
+ *            (N < 8388608 at d = 128): K and V are read through 32-bit
+ *            buffer offsets.
  *   d        head dimension: 64 or 128 (the method needs whole rows of Q and
  *            K on chip, so d must be small: the Triton article's section on
  *            tiled attention).

@@ -38,6 +38,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa355.so")
 
 FA_BF16 = 0
 FA_F32 = 1
+FA_F16 = 2
 
 FA_OK = 0
 FA_ERR_NULL = -1
@@ -149,7 +150,9 @@ def _dtype_code(t):
         return FA_BF16
     if t.dtype == torch.float32:
         return FA_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    if t.dtype == torch.float16:
+        return FA_F16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _prepare(q, k, v, scale, out, lse, stream):

@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0: backward pass
+constexpr int kVersion = 500;  // 0.5.0: fp16 inputs
 constexpr int kMaxSplits = 128;
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
@@ -40,7 +40,7 @@ struct Sizes {
 int check_args(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
                int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, Sizes* sz) {
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
-  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+  if (dtype != FA_BF16 && dtype != FA_F32 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
@@ -53,13 +53,13 @@ int check_args(const void* Q, const void* K, const void* V, void* O, float* L, i
   if (BH > INT_MAX) return FA_ERR_SHAPE;
   const int64_t min_rows_per_block = 32;
   if (BH * ((N + min_rows_per_block - 1) / min_rows_per_block) > INT_MAX) return FA_ERR_SHAPE;
-  const uint64_t esize = dtype == FA_BF16 ? 2 : 4;
+  const uint64_t esize = dtype == FA_F32 ? 4 : 2;
   const uint64_t rows = (uint64_t)BH * (uint64_t)N;
   if (rows > (UINT64_MAX / 4) / ((uint64_t)d * esize)) return FA_ERR_SHAPE;
   const uint64_t tensor_bytes = rows * (uint64_t)d * esize;
-  // The bf16 kernel reads K and V through buffer resources whose size field
+  // The 16-bit kernels read K and V through buffer resources whose size field
   // holds one head (N * d * 2 bytes) as a 32-bit signed count.
-  if (dtype == FA_BF16 && (uint64_t)N * (uint64_t)d * 2 > (uint64_t)INT_MAX) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && (uint64_t)N * (uint64_t)d * 2 > (uint64_t)INT_MAX) return FA_ERR_SHAPE;
   const uint64_t lse_bytes = rows * 4;
 
   const uintptr_t misalign = reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) |
@@ -97,25 +97,25 @@ int64_t bf16_lds_bytes(int64_t N) {
 // The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
 // instance's limit once per process (device-independent attribute) to what
 // its largest launch may use.
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, typename T>
 hipError_t prepare_bf16() {
   static const hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE>),
+      reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE, T>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
       MODE == fa355::kSparse ? kMaxLds : fa355::Bf16Layout<D>::kBytes);
   return status;
 }
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, typename T>
 hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, float* L,
                        int64_t BH, int64_t N, float scale, fa355::ModeArgs sa,
                        hipStream_t stream) {
-  const hipError_t prep = prepare_bf16<D, CAUSAL, MODE>();
+  const hipError_t prep = prepare_bf16<D, CAUSAL, MODE, T>();
   if (prep != hipSuccess) return prep;
   const int num_qtiles = (int)((N + fa355::kBM - 1) / fa355::kBM);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
   const unsigned lds = (unsigned)bf16_lds_bytes<D, MODE>(N);
-  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE>), dim3(total),
+  hipLaunchKernelGGL((fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE, T>), dim3(total),
                      dim3(fa355::kThreads), lds, stream,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), L, (int)N,
@@ -136,17 +136,23 @@ hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, floa
   return hipGetLastError();
 }
 
+template <int MODE, typename T>
+hipError_t launch_mfma(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
+                       int64_t N, int64_t d, float scale, int causal, fa355::ModeArgs sa,
+                       hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_bf16<64, true, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_bf16<64, false, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s);
+  return causal ? launch_bf16<128, true, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s)
+                : launch_bf16<128, false, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s);
+}
+
 template <int MODE>
 hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, float* L,
                           int64_t BH, int64_t N, int64_t d, float scale, int causal, int dtype,
                           fa355::ModeArgs sa, hipStream_t s) {
-  if (dtype == FA_BF16) {
-    if (d == 64)
-      return causal ? launch_bf16<64, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
-                    : launch_bf16<64, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
-    return causal ? launch_bf16<128, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
-                  : launch_bf16<128, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
-  }
+  if (dtype == FA_BF16) return launch_mfma<MODE, __bf16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
+  if (dtype == FA_F16) return launch_mfma<MODE, _Float16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (d == 64)
     return causal ? launch_f32<64, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
                   : launch_f32<64, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
@@ -226,8 +232,11 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
       launch_forward<fa355::kSplit>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, sa, s);
   if (err == hipSuccess) {
     if (dtype == FA_BF16)
-      err = d == 64 ? launch_merge<64, uint16_t>(opart, lpart, O, L, num_splits, sz.rows, s)
-                    : launch_merge<128, uint16_t>(opart, lpart, O, L, num_splits, sz.rows, s);
+      err = d == 64 ? launch_merge<64, __bf16>(opart, lpart, O, L, num_splits, sz.rows, s)
+                    : launch_merge<128, __bf16>(opart, lpart, O, L, num_splits, sz.rows, s);
+    else if (dtype == FA_F16)
+      err = d == 64 ? launch_merge<64, _Float16>(opart, lpart, O, L, num_splits, sz.rows, s)
+                    : launch_merge<128, _Float16>(opart, lpart, O, L, num_splits, sz.rows, s);
     else
       err = d == 64 ? launch_merge<64, float>(opart, lpart, O, L, num_splits, sz.rows, s)
                     : launch_merge<128, float>(opart, lpart, O, L, num_splits, sz.rows, s);
@@ -248,7 +257,7 @@ extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, v
   // The tile list lives in LDS next to the K and V rings.
   const int64_t lds = d == 64 ? bf16_lds_bytes<64, fa355::kSparse>(N)
                               : bf16_lds_bytes<128, fa355::kSparse>(N);
-  if (dtype == FA_BF16 && lds > kMaxLds) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && lds > kMaxLds) return FA_ERR_SHAPE;
   const uint64_t mask_bytes = (uint64_t)mask_heads * (uint64_t)nb * (uint64_t)nb;
   if (ranges_overlap(block_mask, mask_bytes, O, sz.tensor_bytes) ||
       ranges_overlap(block_mask, mask_bytes, L, sz.lse_bytes))
@@ -264,15 +273,15 @@ extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, v
 // ---------------------------------------------------------------------------
 // Backward pass.
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* Dv, void* dQ, void* dK, void* dV,
                            int64_t BH, int64_t N, float scale, hipStream_t s) {
   static const hipError_t attr_kv = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL>),
+      reinterpret_cast<const void*>(&fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL, T>),
       hipFuncAttributeMaxDynamicSharedMemorySize, fa355::BwdKvLayout<D>::kBytes);
   static const hipError_t attr_q = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL>),
+      reinterpret_cast<const void*>(&fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL, T>),
       hipFuncAttributeMaxDynamicSharedMemorySize, fa355::BwdQLayout<D>::kBytes);
   if (attr_kv != hipSuccess) return attr_kv;
   if (attr_q != hipSuccess) return attr_q;
@@ -283,14 +292,14 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const vo
   const auto* g = static_cast<const uint16_t*>(dO);
   const int nk = (int)((N + fa355::kBwdKvKeys - 1) / fa355::kBwdKvKeys);
   const unsigned lds_kv = fa355::BwdKvLayout<D>::kBytes, lds_q = fa355::BwdQLayout<D>::kBytes;
-  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * nk)),
+  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_bf16_kernel<D, CAUSAL, T>), dim3((unsigned)(BH * nk)),
                      dim3(64 * fa355::kBwdKvWaves), lds_kv, s, q, k, v, g, L, Dv,
                      static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), (int)N, (int)BH, scale,
                      c);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nq = (int)((N + fa355::kBM - 1) / fa355::kBM);
-  hipLaunchKernelGGL((fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * nq)),
+  hipLaunchKernelGGL((fa355::fa_bwd_dq_bf16_kernel<D, CAUSAL, T>), dim3((unsigned)(BH * nq)),
                      dim3(fa355::kThreads), lds_q, s, q, k, v, g, L, Dv,
                      static_cast<uint16_t*>(dQ), (int)N, (int)BH, nq, scale, c);
   return hipGetLastError();
@@ -327,6 +336,21 @@ hipError_t launch_bwd_dot(const void* O, const void* dO, float* Dv, uint64_t row
                      dim3(fa355::kDotThreads), 0, s, static_cast<const T*>(O),
                      static_cast<const T*>(dO), Dv, (int64_t)rows);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* L, float* Dv, void* dQ, void* dK, void* dV,
+                           const Sizes& sz, int64_t N, int64_t d, float scale, int causal,
+                           hipStream_t s) {
+  hipError_t err = d == 64 ? launch_bwd_dot<64, T>(O, dO, Dv, sz.rows, s)
+                           : launch_bwd_dot<128, T>(O, dO, Dv, sz.rows, s);
+  if (err != hipSuccess) return err;
+  if (d == 64)
+    return causal ? launch_bwd_bf16<64, true, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                  : launch_bwd_bf16<64, false, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+  return causal ? launch_bwd_bf16<128, true, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                : launch_bwd_bf16<128, false, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
 }
 
 extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -373,18 +397,11 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   (void)hipGetLastError();
   float* Dv = static_cast<float*>(workspace);
   hipError_t err;
-  if (dtype == FA_BF16) {
-    err = d == 64 ? launch_bwd_dot<64, uint16_t>(O, dO, Dv, sz.rows, s)
-                  : launch_bwd_dot<128, uint16_t>(O, dO, Dv, sz.rows, s);
-    if (err == hipSuccess) {
-      if (d == 64)
-        err = causal ? launch_bwd_bf16<64, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
-                     : launch_bwd_bf16<64, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
-      else
-        err = causal ? launch_bwd_bf16<128, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
-                     : launch_bwd_bf16<128, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
-    }
-  } else {
+  if (dtype == FA_BF16)
+    err = launch_bwd_mfma<__bf16>(Q, K, V, O, dO, L, Dv, dQ, dK, dV, sz, N, d, scale, causal, s);
+  else if (dtype == FA_F16)
+    err = launch_bwd_mfma<_Float16>(Q, K, V, O, dO, L, Dv, dQ, dK, dV, sz, N, d, scale, causal, s);
+  else {
     err = d == 64 ? launch_bwd_dot<64, float>(O, dO, Dv, sz.rows, s)
                   : launch_bwd_dot<128, float>(O, dO, Dv, sz.rows, s);
     if (err == hipSuccess) {
@@ -405,7 +422,7 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N is < 1 or too large to index";
     case FA_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
-    case FA_ERR_DTYPE: return "dtype must be FA_BF16 (0) or FA_F32 (1)";
+    case FA_ERR_DTYPE: return "dtype must be FA_BF16 (0), FA_F32 (1) or FA_F16 (2)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "Q, K, V, O must be 16-byte aligned and L 4-byte aligned";
     case FA_ERR_ALIAS: return "O, L or the workspace overlaps another buffer of the call";

@@ -31,13 +31,18 @@ namespace fa355 {
 // D_i = sum_d dO_id O_id in float32, one row per D/8 threads.
 constexpr int kDotThreads = 256;
 
-__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+__device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = __uint_as_float(w[i] << 16);
     x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
+}
+__device__ __forceinline__ void load8(const _Float16* p, float (&x)[8]) {
+  const f16x8 w = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)w[i];
 }
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
@@ -76,35 +81,37 @@ __global__ __launch_bounds__(kDotThreads) void fa_bwd_dot_kernel(const T* __rest
 
 // bf16 B operand of a 32-row MFMA column: elements 16s + 8hh + (0..7) of row
 // `row` (a key of K or V, or a query of Q or dO), s = 0 .. D/16 - 1.
-template <int D>
+template <int D, typename V8>
 __device__ __forceinline__ void load_b_operand(const uint16_t* __restrict__ head, int row, int hh,
-                                               bf16x8 (&f)[D / 16]) {
+                                               V8 (&f)[D / 16]) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
-    f[s] = __builtin_bit_cast(bf16x8,
+    f[s] = __builtin_bit_cast(V8,
                               *reinterpret_cast<const u32x4*>(head + (size_t)row * D + 16 * s + 8 * hh));
 }
 
 // 16-key (or 16-query) step s2 of a 32x64 accumulator pair as a bf16 B operand.
-__device__ __forceinline__ void to_b_operand(const f32x16 (&x)[2], bf16x8 (&f)[kBN / 16]) {
+template <typename T>
+__device__ __forceinline__ void to_b_operand(const f32x16 (&x)[2],
+                                             typename Elem<T>::v8 (&f)[kBN / 16]) {
 #pragma unroll
   for (int s2 = 0; s2 < kBN / 16; ++s2)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[s2][j] = (__bf16)x[s2 >> 1][8 * (s2 & 1) + j];
+    for (int j = 0; j < 8; ++j) f[s2][j] = (T)x[s2 >> 1][8 * (s2 & 1) + j];
 }
 
 // Store a transposed accumulator (lane = row of the output, element 4g+r of
 // block db = column 32db + 8g + 4hh + r) times `mul` as bf16.
-template <int D>
+template <int D, typename T>
 __device__ __forceinline__ void store_rows(uint16_t* __restrict__ out_row, const f32x16 (&acc)[D / 32],
                                           float mul, int hh) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      __bf16 o4[4];
+      T o4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(acc[db][4 * g + r] * mul);
+      for (int r = 0; r < 4; ++r) o4[r] = (T)(acc[db][4 * g + r] * mul);
       *reinterpret_cast<u32x2*>(out_row + 32 * db + 8 * g + 4 * hh) = __builtin_bit_cast(u32x2, o4);
     }
 }
@@ -134,7 +141,7 @@ struct BwdKvLayout {
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T = __bf16>
 __global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -143,6 +150,7 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         float scale, float scale_log2) {
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = BwdKvLayout<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int W = kBwdKvWaves;
   constexpr int kPer = Bf16Layout<D>::kLoadsPerTile / W;  // loads per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -181,7 +189,7 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const size_t head = (size_t)bh * N * D;
 
   // K^T and V^T as B operands (one key per lane), fixed for the workgroup.
-  bf16x8 kf[D / 16], vf[D / 16];
+  V8 kf[D / 16], vf[D / 16];
   load_b_operand<D>(K + head, min(key, N - 1), hh, kf);
   load_b_operand<D>(V + head, min(key, N - 1), hh, vf);
 
@@ -240,8 +248,8 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // S[q][key] and dP[q][key]: element 4g+r of block kb is query
     // q0 + 32kb + key_of_row(8g + 4hh + r).
     f32x16 sacc[2], dpacc[2];
-    score_tile<D>(st + Lay::kOffQk + k_lane, kf, sacc);
-    score_tile<D>(st + Lay::kOffDok + k_lane, vf, dpacc);
+    score_tile<D, T>(st + Lay::kOffQk + k_lane, kf, sacc);
+    score_tile<D, T>(st + Lay::kOffDok + k_lane, vf, dpacc);
 
     // P = exp(scale S - L), dS = P (dP - D); the four queries of a group g
     // are consecutive, so their L and D come as one 16-byte read each.
@@ -269,18 +277,18 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
           dpacc[kb][e] = p * (dpacc[kb][e] - d4[r]);
         }
       }
-    bf16x8 pf[kBN / 16], dsf[kBN / 16];
-    to_b_operand(sacc, pf);
-    to_b_operand(dpacc, dsf);
+    V8 pf[kBN / 16], dsf[kBN / 16];
+    to_b_operand<T>(sacc, pf);
+    to_b_operand<T>(dpacc, dsf);
 
     // dV^T += dO^T P and dK^T += Q^T dS (lane = key).
-    pv_tile<D>(st + Lay::kOffDov + v_lane, pf, dvacc);
-    pv_tile<D>(st + Lay::kOffQv + v_lane, dsf, dkacc);
+    pv_tile<D, T>(st + Lay::kOffDov + v_lane, pf, dvacc);
+    pv_tile<D, T>(st + Lay::kOffQv + v_lane, dsf, dkacc);
   }
 
   if (key < N) {
-    store_rows<D>(dK + head + (size_t)key * D, dkacc, scale, hh);
-    store_rows<D>(dV + head + (size_t)key * D, dvacc, 1.f, hh);
+    store_rows<D, T>(dK + head + (size_t)key * D, dkacc, scale, hh);
+    store_rows<D, T>(dV + head + (size_t)key * D, dvacc, 1.f, hh);
   }
 }
 
@@ -295,7 +303,7 @@ struct BwdQLayout {
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T = __bf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -304,6 +312,7 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                       float scale_log2) {
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = BwdQLayout<D>;
+  using V8 = typename Elem<T>::v8;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -323,7 +332,7 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   if (wq0 < N) my_tiles = ((CAUSAL ? min(N, wq0 + 32) : N) + kBN - 1) / kBN;
 
   // Q^T and dO^T as B operands (one query per lane); this row's L and D.
-  bf16x8 qf[D / 16], dof[D / 16];
+  V8 qf[D / 16], dof[D / 16];
   const int qr = min(qrow, N - 1);
   load_b_operand<D>(Q + head, qr, hh, qf);
   load_b_operand<D>(dO + head, qr, hh, dof);
@@ -369,8 +378,8 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     // S^T[key][q] and dP^T[key][q]: element 4g+r of block kb is key
     // kv0 + 32kb + key_of_row(8g + 4hh + r); lane = query.
     f32x16 sacc[2], dpacc[2];
-    score_tile<D>(st + Lay::kOffKk + k_lane, qf, sacc);
-    score_tile<D>(st + Lay::kOffVk + k_lane, dof, dpacc);
+    score_tile<D, T>(st + Lay::kOffKk + k_lane, qf, sacc);
+    score_tile<D, T>(st + Lay::kOffVk + k_lane, dof, dpacc);
     const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -383,13 +392,13 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         }
         dpacc[kb][e] = p * (dpacc[kb][e] - dq_row);
       }
-    bf16x8 dsf[kBN / 16];
-    to_b_operand(dpacc, dsf);
+    V8 dsf[kBN / 16];
+    to_b_operand<T>(dpacc, dsf);
     // dQ^T += K^T dS^T (K read transposed from its V-style copy).
-    pv_tile<D>(st + Lay::kOffKv + v_lane, dsf, dqacc);
+    pv_tile<D, T>(st + Lay::kOffKv + v_lane, dsf, dqacc);
   }
 
-  if (qrow < N) store_rows<D>(dQ + head + (size_t)qrow * D, dqacc, scale, hh);
+  if (qrow < N) store_rows<D, T>(dQ + head + (size_t)qrow * D, dqacc, scale, hh);
 }
 
 }  // namespace fa355

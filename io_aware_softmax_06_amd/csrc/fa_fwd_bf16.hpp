@@ -230,11 +230,13 @@ struct NoWork {
   __device__ __forceinline__ void operator()(I) const {}
 };
 
-template <int D, int kAhead = 6, typename Work = NoWork>
-__device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D / 16],
+template <int D, typename T = __bf16, int kAheadMax = 6, typename Work = NoWork>
+__device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
                                            f32x16 (&sacc)[2], Work&& work = Work{}) {
   using Lay = Bf16Layout<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
+  constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
   constexpr int kSlots = kAhead + 2;
   u32x4 a[kSlots];
   auto issue = [&](auto ic) {
@@ -253,8 +255,7 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D 
       lds_wait<kMfmas - 1 - i>();
     }
     pin(a[i % kSlots]);
-    sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i % kSlots]),
-                                                         qf[i / 2], sacc[i % 2], 0, 0, 0);
+    sacc[i % 2] = Elem<T>::mfma(__builtin_bit_cast(V8, a[i % kSlots]), qf[i / 2], sacc[i % 2]);
     work(ic);
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -265,12 +266,14 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const bf16x8 (&qf)[D 
 // where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2) [+ 4 for the
 // second read]; the transpose hands lane i the column d0 + i.  vaddr = LDS
 // address of this lane's piece in slab 0, step 0, first read.
-template <int D, int kAhead = 4, typename Work = NoWork>
-__device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN / 16],
+template <int D, typename T = __bf16, int kAheadMax = 4, typename Work = NoWork>
+__device__ __forceinline__ void pv_tile(uint32_t vaddr, const typename Elem<T>::v8 (&pf)[kBN / 16],
                                         f32x16 (&oacc)[D / 32], Work&& work = Work{}) {
   using Lay = Bf16Layout<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int kBlocks = D / 32;
   constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
+  constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
   constexpr int kSlots = kAhead + 2;            // a slot is refilled two MFMAs after its use
   u32x2 v[kSlots][2];
   auto issue = [&](auto ic) {
@@ -294,8 +297,7 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const bf16x8 (&pf)[kBN /
     pin(cur[0]);
     pin(cur[1]);
     const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
-    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[s],
-                                                       oacc[db], 0, 0, 0);
+    oacc[db] = Elem<T>::mfma(__builtin_bit_cast(V8, a), pf[s], oacc[db]);
     work(ic);
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -355,7 +357,7 @@ __device__ __forceinline__ uint32_t lds_read32(uint32_t lds_addr) {
   return v;
 }
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, typename T = __bf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -363,6 +365,7 @@ fa_fwd_bf16_kernel(
     int BH, int num_qtiles, float scale, float scale_log2, ModeArgs split_args) {
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
+  using V8 = typename Elem<T>::v8;  // eight 16-bit elements of type T
   static_assert(D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
@@ -475,13 +478,13 @@ fa_fwd_bf16_kernel(
   const int last = n_tiles - 1;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds d = 16s + 8hh + (0..7).
-  bf16x8 qf[D / 16];
+  V8 qf[D / 16];
   {
     const int qr = min(qrow, N - 1);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       qf[s] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(Qb + (size_t)qr * D + 16 * s + 8 * hh));
+          V8, *reinterpret_cast<const u32x4*>(Qb + (size_t)qr * D + 16 * s + 8 * hh));
   }
 
   f32x16 oacc[D / 32];
@@ -599,7 +602,7 @@ fa_fwd_bf16_kernel(
       st.half_sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
     }
   };
-  auto stage2_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st, bf16x8(&pfo)[kBN / 16]) {
+  auto stage2_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
     constexpr int sidx = decltype(sic)::value;
     if constexpr (sidx < 8) {
       constexpr int e = 2 * sidx;
@@ -617,7 +620,7 @@ fa_fwd_bf16_kernel(
       constexpr int k = sidx - 9;
       constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
 #pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (__bf16)sc[s2 >> 1][8 * (s2 & 1) + j];
+      for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (T)sc[s2 >> 1][8 * (s2 & 1) + j];
     }
   };
   // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
@@ -632,7 +635,7 @@ fa_fwd_bf16_kernel(
   auto stage1 = [&](f32x16(&sc)[2], SoftmaxState& st) {
     static_for<kStage1Steps>([&](auto sic) { stage1_step(sic, sc, st); });
   };
-  auto stage2 = [&](f32x16(&sc)[2], SoftmaxState& st, bf16x8(&pfo)[kBN / 16]) {
+  auto stage2 = [&](f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
     static_for<kStage2Steps>([&](auto sic) { stage2_step(sic, sc, st, pfo); });
   };
   // Empty asm that ties values to this point of the program: the compiler
@@ -651,12 +654,12 @@ fa_fwd_bf16_kernel(
         sc[kb][4 * q + 3] = __uint_as_float(w[3]);
       }
   };
-  auto pin_probs = [&](bf16x8(&pfo)[kBN / 16]) {
+  auto pin_probs = [&](V8(&pfo)[kBN / 16]) {
 #pragma unroll
     for (int s2 = 0; s2 < kBN / 16; ++s2) {
       u32x4 w = __builtin_bit_cast(u32x4, pfo[s2]);
       pin(w);
-      pfo[s2] = __builtin_bit_cast(bf16x8, w);
+      pfo[s2] = __builtin_bit_cast(V8, w);
     }
     asm volatile("" : "+v"(l_run));
   };
@@ -709,10 +712,10 @@ fa_fwd_bf16_kernel(
     block_sync();
 
     f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
-    bf16x8 pf[kBN / 16];  // P^T of the tile whose P V is next
+    V8 pf[kBN / 16];  // P^T of the tile whose P V is next
     if (my_tiles > 0) {
-      score_tile<D>(k_addr(0), qf, sA);
-      score_tile<D>(k_addr(1), qf, sB);
+      score_tile<D, T>(k_addr(0), qf, sA);
+      score_tile<D, T>(k_addr(1), qf, sB);
       mask_tile(e0, sA);
       SoftmaxState st;
       stage1(sA, st);
@@ -757,7 +760,7 @@ fa_fwd_bf16_kernel(
         // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
         // the K load of a later tile in the middle.
         SoftmaxState st;
-        pv_tile<D>(v_addr(svs), pf, oacc, [&](auto ic) {
+        pv_tile<D, T>(v_addr(svs), pf, oacc, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage1Steps>{},
                     [&](auto sic) { stage1_step(sic, cur, st); });
           if constexpr (kShortV && decltype(ic)::value == 0) refill_v(sk, svs, e_v);
@@ -774,7 +777,7 @@ fa_fwd_bf16_kernel(
 
         // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
         // with the V load of a later tile in the middle.
-        score_tile<D>(k_addr(wrap(sk + 2)), qf, nxt, [&](auto ic) {
+        score_tile<D, T>(k_addr(wrap(sk + 2)), qf, nxt, [&](auto ic) {
           run_steps(ic, std::integral_constant<int, kStage2Steps>{},
                     [&](auto sic) { stage2_step(sic, cur, st, pf); });
           if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(sk, svs, e_v);
@@ -783,7 +786,7 @@ fa_fwd_bf16_kernel(
       } else {
         if constexpr (kShortV) refill_v(sk, svs, e_v);
         load_k(wrap(sk + 1), e_k);
-        if (t < my_tiles) pv_tile<D>(v_addr(svs), pf, oacc);
+        if (t < my_tiles) pv_tile<D, T>(v_addr(svs), pf, oacc);
         if constexpr (!kShortV) refill_v(sk, svs, e_v);
       }
 
@@ -837,9 +840,9 @@ fa_fwd_bf16_kernel(
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          __bf16 o4[4];
+          T o4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(oacc[db][4 * g + r] * inv);
+          for (int r = 0; r < 4; ++r) o4[r] = (T)(oacc[db][4 * g + r] * inv);
           *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
               __builtin_bit_cast(u32x2, o4);
         }

@@ -30,8 +30,14 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
 }
 
 template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
+__device__ __forceinline__ void store4<__bf16>(__bf16* p, f32x4 v) {
   __bf16 b[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, b);
+}
+
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* p, f32x4 v) {
+  _Float16 b[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, b);
 }
 

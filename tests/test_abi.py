@@ -93,7 +93,7 @@ def test_unsupported_head_dim(lib, d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED_D
 
 
-@pytest.mark.parametrize("dtype", [-1, 2, 7])
+@pytest.mark.parametrize("dtype", [-1, 3, 7])
 def test_bad_dtype(lib, dtype):
     assert call(dtype=dtype) == fa.FA_ERR_DTYPE
 
@@ -118,6 +118,14 @@ def test_misaligned(lib, over):
                                   dict(L=O + 1024), dict(O=L - 16)])
 def test_aliasing(lib, over):
     assert call(**over) == fa.FA_ERR_ALIAS
+
+
+def test_fp16_shares_the_checks(lib):
+    assert call(dtype=fa.FA_F16, d=96) == fa.FA_ERR_UNSUPPORTED_D
+    assert call(dtype=fa.FA_F16, O=V) == fa.FA_ERR_ALIAS
+    T = 1 << 44
+    far = dict(Q=T, K=2 * T, V=3 * T, O=4 * T, L=5 * T, B=1, H=1)
+    assert call(dtype=fa.FA_F16, N=2**23, d=128, **far) == fa.FA_ERR_SHAPE
 
 
 def test_fp32_shares_the_checks(lib):
@@ -210,6 +218,7 @@ def call_sparse(mask=M, mask_heads=1, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(Q=None), fa.FA_ERR_NULL), (dict(N=0), fa.FA_ERR_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED_D), (dict(dtype=9), fa.FA_ERR_DTYPE),
+    (dict(dtype=fa.FA_F16, d=96), fa.FA_ERR_UNSUPPORTED_D),
     (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(causal=7), fa.FA_ERR_ARG),
     (dict(V=V + 8), fa.FA_ERR_ALIGN), (dict(O=K), fa.FA_ERR_ALIAS)])
 def test_blocksparse_shares_fwd_checks(lib, over, code):

@@ -9,7 +9,8 @@ the backward bench workload, two whole heads.
 Tolerance (no figure is set for gradients, so it follows the arithmetic):
 each of dQ, dK, dV must satisfy max |g - g_ref| <= tol * max |g_ref| with
 tol = 2e-2 for bfloat16 (P and dS enter the products rounded to bf16, 2^-9
-relative, and the outputs are rounded to bf16) and tol = 1e-4 for float32.
+relative, and the outputs are rounded to bf16), 1e-2 for float16 (2^-11) and
+tol = 1e-4 for float32.
 """
 
 import math
@@ -25,7 +26,8 @@ from workloads import make_grad, make_inputs, make_qkv, to_f64_numpy
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 1e-2}
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def _say(msg):
@@ -63,6 +65,8 @@ SMALL = [
     (1, 2, 100, 64, "fp32", True),
     (2, 1, 129, 128, "fp32", False),
     (1, 2, 333, 128, "fp32", True),
+    (1, 2, 300, 128, "fp16", True),
+    (2, 1, 513, 64, "fp16", False),
 ]
 
 
@@ -71,7 +75,7 @@ SMALL = [
 def test_backward_small(gpu_lib, case):
     B, H, N, d, dt, causal = case
     _say(f"[bwd] small {case}")
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tdt = TORCH_DTYPE[dt]
     q, k, v = make_qkv(B, H, N, d, tdt, seed=N + d)
     do = make_grad(B, H, N, d, tdt, seed=N + d)
     scale = 1.0 / math.sqrt(d)

@@ -27,7 +27,8 @@ from workloads import make_inputs, make_qkv, to_f64_numpy
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {"fp32": 1e-4, "bf16": 2e-2}
+TOL_O = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 5e-3}
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 TOL_L = 1e-3
 
 
@@ -79,6 +80,8 @@ SMALL = [
     (1, 1, 100, 64, "fp32", False, "r5"),
     (1, 2, 333, 128, "fp32", True, "r5"),
     (2, 1, 300, 64, "fp32", False, "local"),
+    (1, 2, 700, 128, "fp16", True, "r5"),
+    (1, 1, 1024, 64, "fp16", False, "local"),
 ]
 
 
@@ -88,8 +91,7 @@ def test_blocksparse_small(gpu_lib, case):
     B, H, N, d, dt, causal, kind = case
     _say(f"[sparse] small {case}")
     nb = -(-N // 64)
-    q, k, v = make_qkv(B, H, N, d, torch.bfloat16 if dt == "bf16" else torch.float32,
-                       seed=N + d)
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + d)
     mask = _mask(kind, nb, B, H, seed=N)
     scale = 1.0 / math.sqrt(d)
     O, L = gpu_lib.fwd_blocksparse(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), scale=scale,

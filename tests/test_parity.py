@@ -6,8 +6,9 @@ sizes in the same launch configuration the bench times, and are compared on
 sampled rows that the oracle computes one by one, plus properties checked on
 every row (finite values, each output a convex combination of V's rows).
 
-Tolerances (max-abs): O <= 1e-4 for float32 inputs, <= 2e-2 for bfloat16;
-L <= 1e-3.
+Tolerances (max-abs): O <= 1e-4 for float32 inputs, <= 2e-2 for bfloat16,
+<= 5e-3 for float16 (P and O are rounded to fp16, 2^-11 relative: at most
+2^-11 max|V| + 2^-11 |O| ~ 4e-3 at the workloads' |V| <= 5.6); L <= 1e-3.
 """
 
 import math
@@ -23,7 +24,8 @@ from workloads import make_inputs, make_qkv, to_f64_numpy
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {"fp32": 1e-4, "bf16": 2e-2}
+TOL_O = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 5e-3}
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 TOL_L = 1e-3
 SEEDS = (1, 2, 3)
 
@@ -70,6 +72,10 @@ SMALL = [
     (2, 1, 129, 128, "fp32", True),
     (1, 1, 333, 64, "fp32", True),
     (1, 2, 200, 128, "fp32", False),
+    (1, 1, 1, 64, "fp16", False),
+    (1, 2, 300, 64, "fp16", True),
+    (2, 2, 257, 128, "fp16", True),
+    (1, 1, 1000, 128, "fp16", False),
 ]
 
 
@@ -78,7 +84,7 @@ SMALL = [
 def test_small_shapes(gpu_lib, case):
     B, H, N, d, dt, causal = case
     _say(f"[parity] small {case}")
-    q, k, v = make_qkv(B, H, N, d, torch.bfloat16 if dt == "bf16" else torch.float32, seed=N + d)
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + d)
     scale = 1.0 / math.sqrt(d)
     O, L = run_gpu(gpu_lib, q, k, v, scale, causal)
     compare_full(O, L, q, k, v, scale, causal, dt)
@@ -252,3 +258,33 @@ def test_error_status_raises(gpu_lib):
     with pytest.raises(gpu_lib.FaError) as ei:
         gpu_lib.fwd(q, q.clone(), q.clone())
     assert ei.value.status == gpu_lib.FA_ERR_UNSUPPORTED_D
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_at_causal_workload_shape(gpu_lib, causal):
+    """float16 inputs at B=2 H=32 N=4096 d=128, sampled rows against the oracle."""
+    w = workloads.CAUSAL_4K
+    _say(f"[parity] fp16 at {w.describe()} causal={causal}")
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, torch.float16, seed=3)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    O, L = gpu_lib.fwd(qd, kd, vd, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    check_every_row(O, L, vd)
+    rng = np.random.default_rng(3)
+    rows = _sample_rows(w, rng)
+    idx = torch.tensor(rows, dtype=torch.long)
+    Og = O[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+    Lg = L[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+    Or, Lr = oracle.attention_rows(to_f64_numpy(q), to_f64_numpy(k), to_f64_numpy(v), w.scale,
+                                   causal, rows)
+    eo, el = np.abs(Og - Or).max(), np.abs(Lg - Lr).max()
+    _say(f"[parity]   rows={len(rows)} max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= TOL_O["fp16"] and el <= TOL_L
+
+
+def test_fp16_large_logits(gpu_lib):
+    """Logits of several hundred: the exponentials are float32, so fp16 inputs do not overflow."""
+    _say("[parity] fp16 stress logits")
+    q, k, v = make_qkv(2, 2, 333, 64, torch.float16, seed=5, stress=True)
+    O, L = run_gpu(gpu_lib, q, k, v, 0.125, False)
+    compare_full(O, L, q, k, v, 0.125, False, "fp16")

@@ -27,7 +27,8 @@ from workloads import make_inputs, make_qkv, to_f64_numpy
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {"fp32": 1e-4, "bf16": 2e-2}
+TOL_O = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 5e-3}
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 TOL_L = 1e-3
 
 
@@ -89,6 +90,8 @@ SMALL = [
     (1, 2, 333, 128, "fp32", True, 3),
     (1, 1, 65, 64, "fp32", False, 5),
     (2, 1, 700, 64, "fp32", True, 7),
+    (1, 2, 513, 128, "fp16", True, 3),
+    (2, 1, 300, 64, "fp16", False, 4),
 ]
 
 
@@ -97,8 +100,7 @@ SMALL = [
 def test_split_small(gpu_lib, case):
     B, H, N, d, dt, causal, S = case
     _say(f"[splitkv] small {case}")
-    q, k, v = make_qkv(B, H, N, d, torch.bfloat16 if dt == "bf16" else torch.float32,
-                       seed=N + d + S)
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + d + S)
     scale = 1.0 / math.sqrt(d)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     O, L, ws = gpu_lib.fwd_splitkv(qd, kd, vd, S, scale=scale, causal=causal)
