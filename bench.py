@@ -300,7 +300,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_launch_s / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_F32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS  # fp16 MFMA: same peak
     props = torch.cuda.get_device_properties(dev)
     print(f"device: {props.name}, {props.multi_processor_count} CUs; kernel avg "
           f"{avg_launch_s * 1e6:.1f} us (min {min(launch_ms) * 1e3:.1f} us), "

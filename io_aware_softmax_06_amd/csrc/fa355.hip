@@ -42,7 +42,7 @@ int check_args(const void* Q, const void* K, const void* V, void* O, float* L, i
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
   if (dtype != FA_BF16 && dtype != FA_F32 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
 
@@ -126,7 +126,7 @@ hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, flo
 template <int D, bool CAUSAL, int MODE>
 hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
                       int64_t N, float scale, fa355::ModeArgs sa, hipStream_t stream) {
-  constexpr int kRows = 64 / (D / 64);
+  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;
   const int num_qtiles = (int)((N + kRows - 1) / kRows);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
   hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, MODE>), dim3(total), dim3(64), 0,
@@ -140,6 +140,9 @@ template <int MODE, typename T>
 hipError_t launch_mfma(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
                        int64_t N, int64_t d, float scale, int causal, fa355::ModeArgs sa,
                        hipStream_t s) {
+  if (d == 32)
+    return causal ? launch_bf16<32, true, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_bf16<32, false, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s);
   if (d == 64)
     return causal ? launch_bf16<64, true, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s)
                   : launch_bf16<64, false, MODE, T>(Q, K, V, O, L, BH, N, scale, sa, s);
@@ -153,6 +156,9 @@ hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, 
                           fa355::ModeArgs sa, hipStream_t s) {
   if (dtype == FA_BF16) return launch_mfma<MODE, __bf16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (dtype == FA_F16) return launch_mfma<MODE, _Float16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
+  if (d == 32)
+    return causal ? launch_f32<32, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_f32<32, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
   if (d == 64)
     return causal ? launch_f32<64, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
                   : launch_f32<64, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
@@ -171,6 +177,14 @@ hipError_t launch_merge(const float* opart, const float* lpart, void* O, float* 
                      dim3(fa355::kMergeThreads), 0, s, opart, lpart, static_cast<OutT*>(O), L, S,
                      (int64_t)rows);
   return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_merge_d(const float* opart, const float* lpart, void* O, float* L, int S,
+                          uint64_t rows, int64_t d, hipStream_t s) {
+  if (d == 32) return launch_merge<32, OutT>(opart, lpart, O, L, S, rows, s);
+  if (d == 64) return launch_merge<64, OutT>(opart, lpart, O, L, S, rows, s);
+  return launch_merge<128, OutT>(opart, lpart, O, L, S, rows, s);
 }
 
 }  // namespace
@@ -194,7 +208,7 @@ extern "C" int64_t fa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int
   if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
     return FA_ERR_SHAPE;
   if (B * H > INT_MAX) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
   const uint64_t bytes = split_workspace_bytes((uint64_t)(B * H) * (uint64_t)N, d, num_splits);
   if (bytes == 0 || bytes > (uint64_t)INT64_MAX) return FA_ERR_SHAPE;
@@ -232,14 +246,11 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
       launch_forward<fa355::kSplit>(Q, K, V, O, L, sz.BH, N, d, scale, causal, dtype, sa, s);
   if (err == hipSuccess) {
     if (dtype == FA_BF16)
-      err = d == 64 ? launch_merge<64, __bf16>(opart, lpart, O, L, num_splits, sz.rows, s)
-                    : launch_merge<128, __bf16>(opart, lpart, O, L, num_splits, sz.rows, s);
+      err = launch_merge_d<__bf16>(opart, lpart, O, L, num_splits, sz.rows, d, s);
     else if (dtype == FA_F16)
-      err = d == 64 ? launch_merge<64, _Float16>(opart, lpart, O, L, num_splits, sz.rows, s)
-                    : launch_merge<128, _Float16>(opart, lpart, O, L, num_splits, sz.rows, s);
+      err = launch_merge_d<_Float16>(opart, lpart, O, L, num_splits, sz.rows, d, s);
     else
-      err = d == 64 ? launch_merge<64, float>(opart, lpart, O, L, num_splits, sz.rows, s)
-                    : launch_merge<128, float>(opart, lpart, O, L, num_splits, sz.rows, s);
+      err = launch_merge_d<float>(opart, lpart, O, L, num_splits, sz.rows, d, s);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -255,8 +266,9 @@ extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, v
   if (mask_heads != 1 && mask_heads != H && mask_heads != sz.BH) return FA_ERR_ARG;
   const int64_t nb = (N + fa355::kMaskBlock - 1) / fa355::kMaskBlock;
   // The tile list lives in LDS next to the K and V rings.
-  const int64_t lds = d == 64 ? bf16_lds_bytes<64, fa355::kSparse>(N)
-                              : bf16_lds_bytes<128, fa355::kSparse>(N);
+  const int64_t lds = d == 32   ? bf16_lds_bytes<32, fa355::kSparse>(N)
+                      : d == 64 ? bf16_lds_bytes<64, fa355::kSparse>(N)
+                                : bf16_lds_bytes<128, fa355::kSparse>(N);
   if (dtype != FA_F32 && lds > kMaxLds) return FA_ERR_SHAPE;
   const uint64_t mask_bytes = (uint64_t)mask_heads * (uint64_t)nb * (uint64_t)nb;
   if (ranges_overlap(block_mask, mask_bytes, O, sz.tensor_bytes) ||
@@ -309,7 +321,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const void* dO,
                           const float* L, const float* Dv, void* dQ, void* dK, void* dV,
                           int64_t BH, int64_t N, float scale, hipStream_t s) {
-  constexpr int kRows = 64 / (D / 64);
+  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;
   const float c = scale * fa355::kLog2e;
   const auto* q = static_cast<const float*>(Q);
   const auto* k = static_cast<const float*>(K);
@@ -343,9 +355,13 @@ hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const vo
                            const void* dO, const float* L, float* Dv, void* dQ, void* dK, void* dV,
                            const Sizes& sz, int64_t N, int64_t d, float scale, int causal,
                            hipStream_t s) {
-  hipError_t err = d == 64 ? launch_bwd_dot<64, T>(O, dO, Dv, sz.rows, s)
-                           : launch_bwd_dot<128, T>(O, dO, Dv, sz.rows, s);
+  hipError_t err = d == 32   ? launch_bwd_dot<32, T>(O, dO, Dv, sz.rows, s)
+                   : d == 64 ? launch_bwd_dot<64, T>(O, dO, Dv, sz.rows, s)
+                             : launch_bwd_dot<128, T>(O, dO, Dv, sz.rows, s);
   if (err != hipSuccess) return err;
+  if (d == 32)
+    return causal ? launch_bwd_bf16<32, true, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                  : launch_bwd_bf16<32, false, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
   if (d == 64)
     return causal ? launch_bwd_bf16<64, true, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
                   : launch_bwd_bf16<64, false, T>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
@@ -357,7 +373,7 @@ extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) 
   if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
     return FA_ERR_SHAPE;
   if (B * H > INT_MAX) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   return B * H * N * 4;
 }
 
@@ -402,10 +418,14 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   else if (dtype == FA_F16)
     err = launch_bwd_mfma<_Float16>(Q, K, V, O, dO, L, Dv, dQ, dK, dV, sz, N, d, scale, causal, s);
   else {
-    err = d == 64 ? launch_bwd_dot<64, float>(O, dO, Dv, sz.rows, s)
-                  : launch_bwd_dot<128, float>(O, dO, Dv, sz.rows, s);
+    err = d == 32   ? launch_bwd_dot<32, float>(O, dO, Dv, sz.rows, s)
+          : d == 64 ? launch_bwd_dot<64, float>(O, dO, Dv, sz.rows, s)
+                    : launch_bwd_dot<128, float>(O, dO, Dv, sz.rows, s);
     if (err == hipSuccess) {
-      if (d == 64)
+      if (d == 32)
+        err = causal ? launch_bwd_f32<32, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
+                     : launch_bwd_f32<32, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
+      else if (d == 64)
         err = causal ? launch_bwd_f32<64, true>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s)
                      : launch_bwd_f32<64, false>(Q, K, V, dO, L, Dv, dQ, dK, dV, sz.BH, N, scale, s);
       else
@@ -421,7 +441,7 @@ extern "C" const char* fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N is < 1 or too large to index";
-    case FA_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
+    case FA_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_BF16 (0), FA_F32 (1) or FA_F16 (2)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "Q, K, V, O must be 16-byte aligned and L 4-byte aligned";

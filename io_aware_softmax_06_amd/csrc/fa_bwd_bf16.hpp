@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kDotThreads) void fa_bwd_dot_kernel(const T* __rest
                                                                  const T* __restrict__ dO,
                                                                  float* __restrict__ Dv,
                                                                  int64_t rows) {
-  constexpr int kPer = D / 8;  // threads per row: 8 or 16, a power of two inside one wave
+  constexpr int kPer = D / 8;  // threads per row: 4, 8 or 16, a power of two inside one wave
   constexpr int kRowsPer = kDotThreads / kPer;
   const int c = threadIdx.x % kPer;
   const int64_t stride = (int64_t)gridDim.x * kRowsPer;
@@ -148,11 +148,12 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const float* __restrict__ Lse, const float* __restrict__ Dv,
                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH,
                         float scale, float scale_log2) {
-  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
   using Lay = BwdKvLayout<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int W = kBwdKvWaves;
   constexpr int kPer = Bf16Layout<D>::kLoadsPerTile / W;  // loads per wave per tile
+  static_assert(kPer >= 1, "every wave loads a piece of every tile");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -310,7 +311,7 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                       const float* __restrict__ Lse, const float* __restrict__ Dv,
                       uint16_t* __restrict__ dQ, int N, int BH, int num_qtiles, float scale,
                       float scale_log2) {
-  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
   using Lay = BwdQLayout<D>;
   using V8 = typename Elem<T>::v8;
   extern __shared__ __attribute__((aligned(16))) char smem[];

@@ -14,12 +14,18 @@ namespace fa355 {
 
 constexpr int kBwdF32Rows = 32;  // streamed rows per staged tile
 
+// Components of d per lane: all of a row when d <= 64, else 64 (two lanes per
+// row at d = 128).
 template <int D>
-__device__ __forceinline__ float dot_row(const f32x4 (&a)[16], const f32x4* b, int part) {
+constexpr int kBwdDl = D >= 64 ? 64 : D;
+
+template <int D>
+__device__ __forceinline__ float dot_row(const f32x4 (&a)[kBwdDl<D> / 4], const f32x4* b, int part) {
+  constexpr int kT = kBwdDl<D> / 4;
   float acc = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const f32x4 x = b[part * 16 + t];
+  for (int t = 0; t < kT; ++t) {
+    const f32x4 x = b[part * kT + t];
     acc = __builtin_fmaf(a[t][0], x[0], acc);
     acc = __builtin_fmaf(a[t][1], x[1], acc);
     acc = __builtin_fmaf(a[t][2], x[2], acc);
@@ -36,8 +42,9 @@ __global__ __launch_bounds__(64) void fa_bwd_dkdv_f32_kernel(
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dv,
     float* __restrict__ dK, float* __restrict__ dV, int N, int num_ktiles, float scale,
     float scale_log2) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  constexpr int kRows = 64 / (D / 64);
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;
+  constexpr int kT = kBwdDl<D> / 4;  // f32x4 pieces of d per lane
   __shared__ f32x4 qs[kBwdF32Rows][D / 4];
   __shared__ f32x4 ds_[kBwdF32Rows][D / 4];
   __shared__ float ls[kBwdF32Rows], dls[kBwdF32Rows];
@@ -49,12 +56,12 @@ __global__ __launch_bounds__(64) void fa_bwd_dkdv_f32_kernel(
   const int key = k0 + lane % kRows;
   const size_t head = (size_t)bh * N * D;
 
-  f32x4 k[16], v[16], dk[16], dv[16];
+  f32x4 k[kT], v[kT], dk[kT], dv[kT];
   const int kr = min(key, N - 1);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    k[t] = *reinterpret_cast<const f32x4*>(K + head + (size_t)kr * D + part * 64 + 4 * t);
-    v[t] = *reinterpret_cast<const f32x4*>(V + head + (size_t)kr * D + part * 64 + 4 * t);
+  for (int t = 0; t < kT; ++t) {
+    k[t] = *reinterpret_cast<const f32x4*>(K + head + (size_t)kr * D + part * kBwdDl<D> + 4 * t);
+    v[t] = *reinterpret_cast<const f32x4*>(V + head + (size_t)kr * D + part * kBwdDl<D> + 4 * t);
     dk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     dv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -88,17 +95,17 @@ __global__ __launch_bounds__(64) void fa_bwd_dkdv_f32_kernel(
       const float dp = dot_row<D>(v, ds_[i], part);
       const float dsv = p * (dp - dls[i]);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        dv[t] += p * ds_[i][part * 16 + t];
-        dk[t] += dsv * qs[i][part * 16 + t];
+      for (int t = 0; t < kT; ++t) {
+        dv[t] += p * ds_[i][part * kT + t];
+        dk[t] += dsv * qs[i][part * kT + t];
       }
     }
   }
   if (key < N) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      *reinterpret_cast<f32x4*>(dK + head + (size_t)key * D + part * 64 + 4 * t) = dk[t] * scale;
-      *reinterpret_cast<f32x4*>(dV + head + (size_t)key * D + part * 64 + 4 * t) = dv[t];
+    for (int t = 0; t < kT; ++t) {
+      *reinterpret_cast<f32x4*>(dK + head + (size_t)key * D + part * kBwdDl<D> + 4 * t) = dk[t] * scale;
+      *reinterpret_cast<f32x4*>(dV + head + (size_t)key * D + part * kBwdDl<D> + 4 * t) = dv[t];
     }
   }
 }
@@ -109,8 +116,9 @@ __global__ __launch_bounds__(64) void fa_bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dv,
     float* __restrict__ dQ, int N, int num_qtiles, float scale, float scale_log2) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  constexpr int kRows = 64 / (D / 64);
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;
+  constexpr int kT = kBwdDl<D> / 4;  // f32x4 pieces of d per lane
   __shared__ f32x4 ks[kBwdF32Rows][D / 4];
   __shared__ f32x4 vs[kBwdF32Rows][D / 4];
 
@@ -123,12 +131,12 @@ __global__ __launch_bounds__(64) void fa_bwd_dq_f32_kernel(
   const int qrow = q0 + lane % kRows;
   const size_t head = (size_t)bh * N * D;
 
-  f32x4 q[16], g[16], dq[16];
+  f32x4 q[kT], g[kT], dq[kT];
   const int qr = min(qrow, N - 1);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    q[t] = *reinterpret_cast<const f32x4*>(Q + head + (size_t)qr * D + part * 64 + 4 * t);
-    g[t] = *reinterpret_cast<const f32x4*>(dO + head + (size_t)qr * D + part * 64 + 4 * t);
+  for (int t = 0; t < kT; ++t) {
+    q[t] = *reinterpret_cast<const f32x4*>(Q + head + (size_t)qr * D + part * kBwdDl<D> + 4 * t);
+    g[t] = *reinterpret_cast<const f32x4*>(dO + head + (size_t)qr * D + part * kBwdDl<D> + 4 * t);
     dq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float lq = Lse[(size_t)bh * N + qr];
@@ -158,13 +166,13 @@ __global__ __launch_bounds__(64) void fa_bwd_dq_f32_kernel(
       const float dp = dot_row<D>(g, vs[j], part);
       const float dsv = p * (dp - drow);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) dq[t] += dsv * ks[j][part * 16 + t];
+      for (int t = 0; t < kT; ++t) dq[t] += dsv * ks[j][part * kT + t];
     }
   }
   if (qrow < N) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      *reinterpret_cast<f32x4*>(dQ + head + (size_t)qrow * D + part * 64 + 4 * t) = dq[t] * scale;
+    for (int t = 0; t < kT; ++t)
+      *reinterpret_cast<f32x4*>(dQ + head + (size_t)qrow * D + part * kBwdDl<D> + 4 * t) = dq[t] * scale;
   }
 }
 

@@ -89,8 +89,10 @@ struct Bf16Layout {
   static constexpr int kBytes = (kStages + kVStages) * kTileBytes;  // 16 KB per slot at d = 128
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
   static constexpr int kLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
-  static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
-  static_assert(kLoadsPerWave >= 1 && kLoadsPerTile % kWaves == 0, "tile split over waves");
+  // Loads per wave; at d = 32 a tile is 4 KB, fewer pieces than waves, and
+  // only the first kLoadsPerTile waves load (one piece each).
+  static constexpr int kLoadsPerWave = kLoadsPerTile >= kWaves ? kLoadsPerTile / kWaves : 1;
+  static_assert(kLoadsPerTile % kWaves == 0 || kWaves % kLoadsPerTile == 0, "tile split over waves");
 };
 
 // Key (within a 32-key block) fed to A-operand row i of the score MFMA.  With
@@ -184,7 +186,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_resource(const uint16_t* 
 template <int D, bool IS_V, int W = kWaves>
 __device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane, int r) {
   using Lay = Bf16Layout<D>;
-  const int slice = wave * (Lay::kLoadsPerTile / W) + r;
+  constexpr int kPer = Lay::kLoadsPerTile >= W ? Lay::kLoadsPerTile / W : 1;
+  const int slice = min(wave * kPer + r, Lay::kLoadsPerTile - 1);  // waves that load nothing
   int row, col;
   if (IS_V) {  // slab db = slice / 4 holds rows 16 (slice % 4) .. +15
     row = 16 * (slice & 3) + (lane >> 2);
@@ -203,8 +206,9 @@ __device__ __forceinline__ void load_tile_direct(char* smem, int buf_off,
                                                  __amdgpu_buffer_rsrc_t rsrc, int kv0, int wave,
                                                  const uint32_t* lane_off) {
   using Lay = Bf16Layout<D>;
-  constexpr int kPer = Lay::kLoadsPerTile / W;
-  static_assert(kPer >= 1 && Lay::kLoadsPerTile % W == 0, "tile split over waves");
+  constexpr int kPer = Lay::kLoadsPerTile >= W ? Lay::kLoadsPerTile / W : 1;
+  static_assert(Lay::kLoadsPerTile % W == 0 || W % Lay::kLoadsPerTile == 0, "tile split over waves");
+  if (Lay::kLoadsPerTile < W && wave >= Lay::kLoadsPerTile) return;  // (uniform per wave)
   const uint32_t tile_off = (uint32_t)kv0 * (D * 2);
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
@@ -366,7 +370,7 @@ fa_fwd_bf16_kernel(
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
   using V8 = typename Elem<T>::v8;  // eight 16-bit elements of type T
-  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
   constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)

@@ -22,12 +22,12 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ Lse, int N, int BH, int num_qtiles, float scale,
     float scale_log2, ModeArgs split_args) {
-  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
-  constexpr int kLanesPerRow = D / 64;
+  constexpr int kLanesPerRow = D >= 64 ? D / 64 : 1;
   constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
-  constexpr int kDl = 64;                   // components of d held per lane
+  constexpr int kDl = D / kLanesPerRow;     // components of d held per lane
   __shared__ f32x4 ks[kF32Keys][D / 4];
   __shared__ f32x4 vs[kF32Keys][D / 4];
 

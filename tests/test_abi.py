@@ -88,7 +88,7 @@ def test_bf16_head_must_fit_32bit_offsets(lib):
     assert call(N=2**24, d=64, **far) == fa.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 1, 32, 63, 65, 96, 127, 129, 256])
+@pytest.mark.parametrize("d", [0, 1, 16, 31, 33, 63, 65, 96, 127, 129, 512])
 def test_unsupported_head_dim(lib, d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED_D
 
@@ -168,7 +168,7 @@ def call_split(S=4, ws=W, ws_bytes_=None, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(Q=None), fa.FA_ERR_NULL), (dict(L=None), fa.FA_ERR_NULL),
-    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=48), fa.FA_ERR_UNSUPPORTED_D),
     (dict(dtype=5), fa.FA_ERR_DTYPE), (dict(scale=math.nan), fa.FA_ERR_SCALE),
     (dict(causal=3), fa.FA_ERR_ARG), (dict(K=K + 4), fa.FA_ERR_ALIGN),
     (dict(O=V), fa.FA_ERR_ALIAS)])
@@ -266,7 +266,7 @@ def test_bwd_null(lib, field):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED_D),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=48), fa.FA_ERR_UNSUPPORTED_D),
     (dict(dtype=3), fa.FA_ERR_DTYPE), (dict(scale=-1.0), fa.FA_ERR_SCALE),
     (dict(causal=2), fa.FA_ERR_ARG), (dict(dO=DO + 8), fa.FA_ERR_ALIGN),
     (dict(dK=GK + 2), fa.FA_ERR_ALIGN), (dict(L=L + 1), fa.FA_ERR_ALIGN)])

@@ -67,6 +67,9 @@ SMALL = [
     (1, 2, 333, 128, "fp32", True),
     (1, 2, 300, 128, "fp16", True),
     (2, 1, 513, 64, "fp16", False),
+    (1, 2, 300, 32, "bf16", True),
+    (2, 1, 129, 32, "bf16", False),
+    (1, 2, 100, 32, "fp32", True),
 ]
 
 

@@ -82,6 +82,8 @@ SMALL = [
     (2, 1, 300, 64, "fp32", False, "local"),
     (1, 2, 700, 128, "fp16", True, "r5"),
     (1, 1, 1024, 64, "fp16", False, "local"),
+    (1, 2, 777, 32, "bf16", True, "r5"),
+    (1, 1, 200, 32, "fp32", False, "r5"),
 ]
 
 

@@ -76,6 +76,12 @@ SMALL = [
     (1, 2, 300, 64, "fp16", True),
     (2, 2, 257, 128, "fp16", True),
     (1, 1, 1000, 128, "fp16", False),
+    (1, 1, 1, 32, "bf16", False),
+    (1, 2, 300, 32, "bf16", True),
+    (2, 1, 1000, 32, "bf16", False),
+    (1, 2, 129, 32, "fp16", True),
+    (1, 1, 100, 32, "fp32", False),
+    (1, 2, 333, 32, "fp32", True),
 ]
 
 

@@ -92,6 +92,8 @@ SMALL = [
     (2, 1, 700, 64, "fp32", True, 7),
     (1, 2, 513, 128, "fp16", True, 3),
     (2, 1, 300, 64, "fp16", False, 4),
+    (1, 2, 700, 32, "bf16", True, 3),
+    (1, 1, 300, 32, "fp32", False, 2),
 ]
 
 

@@ -28,7 +28,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp16"
     causal: bool
     stress: bool = False
 
@@ -38,7 +38,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+        return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[self.dtype]
 
     def describe(self) -> str:
         mask = "causal" if self.causal else "non-causal"
@@ -155,3 +155,12 @@ def make_grad(B, H, N, d, dtype, seed, device="cpu"):
 # The backward workload: the causal shape B=2, H=32, N=4096, d=128 in bf16.
 BWD_CAUSAL_4K = Workload("bwd_causal_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf16", True)
 BY_NAME[BWD_CAUSAL_4K.name] = BWD_CAUSAL_4K
+
+
+# More element types and head dimensions: the causal shape in fp16, and
+# d = 32 at B=4, H=32, N=2048 (the same number of heads times rows as the
+# multi-head workload's twice over).
+CAUSAL_4K_FP16 = Workload("causal_fp16_b2h32n4096d128", 2, 32, 4096, 128, "fp16", True)
+MHA_D32 = Workload("mha_bf16_b4h32n2048d32", 4, 32, 2048, 32, "bf16", False)
+for _w in (CAUSAL_4K_FP16, MHA_D32):
+    BY_NAME[_w.name] = _w
