@@ -39,7 +39,8 @@ typedef enum {
   FA_ERR_SHAPE = -2,          /* B, H or N < 1, or a size too large to index
                                  (bf16, fp16: one head of K, N * d * 2 bytes,
                                  must be below 2^31) */
-  FA_ERR_UNSUPPORTED_D = -3,  /* head dimension d is not 32, 64 or 128 */
+  FA_ERR_UNSUPPORTED_D = -3,  /* head dimension d is not 32, 64, 128 or 256
+                                 (block-sparse and backward: not 32, 64, 128) */
   FA_ERR_DTYPE = -4,          /* dtype is not an fa_dtype value */
   FA_ERR_SCALE = -5,          /* scale is not finite or not > 0 */
   FA_ERR_ALIGN = -6,          /* Q, K, V or O not 16-byte aligned, or L not 4-byte aligned */
@@ -63,9 +64,9 @@ typedef enum {
  *            With FA_BF16 or FA_F16, N * d * 2 must be below 2^31
  *            (N < 8388608 at d = 128): K and V are read through 32-bit
  *            buffer offsets.
- *   d        head dimension: 32, 64 or 128 (the method needs whole rows of Q
- *            and K on chip, so d must be small: the Triton article's section
- *            on tiled attention).
+ *   d        head dimension: 32, 64, 128 or 256 (the method needs whole rows
+ *            of Q and K on chip, so d must be small: the Triton article's
+ *            section on tiled attention).
  *   scale    multiplier of the scores, finite and > 0 (usually 1/sqrt(d)).
  *   causal   0: every key visible; 1: key j visible to query i iff j <= i.
  *   stream   HIP stream (a hipStream_t passed as void*; NULL = null stream).

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa355.so")
-SOURCES = [os.path.join(CSRC, "fa355.hip")]
+SOURCES = [os.path.join(CSRC, "fa355.hip"), os.path.join(CSRC, "fa355_d256.hip")]
 DEPENDS = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, "fa355.h")]
 
 HIPCC_FLAGS = [
@@ -44,20 +44,41 @@ def hipcc_path():
 
 
 def build(verbose=False, extra_flags=()):
-    """Compile libfa355.so; returns its path.  Raises on a compiler error."""
+    """Compile libfa355.so; returns its path.  Raises on a compiler error.
+
+    Each translation unit is compiled to an object in parallel, then one
+    link step makes the shared library."""
+    hipcc = hipcc_path()
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(PKG_DIR, "_build", os.path.basename(src) + ".o")
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        cmd = [hipcc, *[f for f in HIPCC_FLAGS if f != "-shared"], *extra_flags, "-c",
+               "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True))
+        objs.append(obj)
+    # hipcc's host pass does not know the packed-fp32 feature; drop that note.
+    noise = "is not a recognized feature for this target"
+    errors = []
+    for p in procs:
+        _, err = p.communicate()
+        err = "\n".join(line for line in err.splitlines() if noise not in line)
+        if p.returncode != 0:
+            errors.append(err)
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
-           *SOURCES, "-o", tmp]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature; drop that note.
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

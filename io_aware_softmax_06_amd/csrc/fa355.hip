@@ -16,6 +16,7 @@
 #include "fa_merge.hpp"
 #include "fa_bwd_bf16.hpp"
 #include "fa_bwd_f32.hpp"
+#include "fa355_d256.h"
 
 namespace {
 
@@ -42,7 +43,7 @@ int check_args(const void* Q, const void* K, const void* V, void* O, float* L, i
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
   if (dtype != FA_BF16 && dtype != FA_F32 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_D;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
 
@@ -126,7 +127,7 @@ hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, flo
 template <int D, bool CAUSAL, int MODE>
 hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
                       int64_t N, float scale, fa355::ModeArgs sa, hipStream_t stream) {
-  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;
+  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;  // 16 rows at d = 256
   const int num_qtiles = (int)((N + kRows - 1) / kRows);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
   hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, MODE>), dim3(total), dim3(64), 0,
@@ -154,6 +155,14 @@ template <int MODE>
 hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, float* L,
                           int64_t BH, int64_t N, int64_t d, float scale, int causal, int dtype,
                           fa355::ModeArgs sa, hipStream_t s) {
+  if (d == 256 && dtype != FA_F32) {
+    return fa355_d256_forward(Q, K, V, O, L, BH, N, scale, causal, dtype == FA_F16 ? 1 : 0,
+                              sa.num_splits, MODE == fa355::kSplit ? sa.opart : nullptr,
+                              sa.lpart, s);
+  }
+  if (d == 256)
+    return causal ? launch_f32<256, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
+                  : launch_f32<256, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
   if (dtype == FA_BF16) return launch_mfma<MODE, __bf16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (dtype == FA_F16) return launch_mfma<MODE, _Float16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (d == 32)
@@ -183,6 +192,7 @@ template <typename OutT>
 hipError_t launch_merge_d(const float* opart, const float* lpart, void* O, float* L, int S,
                           uint64_t rows, int64_t d, hipStream_t s) {
   if (d == 32) return launch_merge<32, OutT>(opart, lpart, O, L, S, rows, s);
+  if (d == 256) return launch_merge<256, OutT>(opart, lpart, O, L, S, rows, s);
   if (d == 64) return launch_merge<64, OutT>(opart, lpart, O, L, S, rows, s);
   return launch_merge<128, OutT>(opart, lpart, O, L, S, rows, s);
 }
@@ -208,7 +218,7 @@ extern "C" int64_t fa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int
   if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
     return FA_ERR_SHAPE;
   if (B * H > INT_MAX) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_D;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
   const uint64_t bytes = split_workspace_bytes((uint64_t)(B * H) * (uint64_t)N, d, num_splits);
   if (bytes == 0 || bytes > (uint64_t)INT64_MAX) return FA_ERR_SHAPE;
@@ -262,6 +272,7 @@ extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, v
   Sizes sz;
   const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
   if (rc != FA_OK) return rc;
+  if (d == 256) return FA_ERR_UNSUPPORTED_D;  // the rings fill the LDS: no room for the list
   if (!block_mask) return FA_ERR_NULL;
   if (mask_heads != 1 && mask_heads != H && mask_heads != sz.BH) return FA_ERR_ARG;
   const int64_t nb = (N + fa355::kMaskBlock - 1) / fa355::kMaskBlock;
@@ -373,7 +384,7 @@ extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) 
   if (B < 1 || H < 1 || N < 1 || B > INT_MAX || H > INT_MAX || N > INT_MAX - 256)
     return FA_ERR_SHAPE;
   if (B * H > INT_MAX) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;  // backward: d <= 128
   return B * H * N * 4;
 }
 
@@ -389,6 +400,7 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   const int rc = check_args(Q, K, V, const_cast<void*>(O), const_cast<float*>(L), B, H, N, d,
                             scale, causal, dtype, &sz);
   if (rc != FA_OK) return rc;
+  if (d == 256) return FA_ERR_UNSUPPORTED_D;  // backward: d <= 128
   const uintptr_t misalign = reinterpret_cast<uintptr_t>(dO) | reinterpret_cast<uintptr_t>(dQ) |
                              reinterpret_cast<uintptr_t>(dK) | reinterpret_cast<uintptr_t>(dV);
   if ((misalign & 15u) != 0) return FA_ERR_ALIGN;
@@ -441,7 +453,8 @@ extern "C" const char* fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N is < 1 or too large to index";
-    case FA_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128";
+    case FA_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64, 128 or 256 (the "
+                                      "backward and block-sparse paths: 32, 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_BF16 (0), FA_F32 (1) or FA_F16 (2)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "Q, K, V, O must be 16-byte aligned and L 4-byte aligned";

@@ -25,7 +25,7 @@
 
 #include "fa_fwd_bf16.hpp"
 
-namespace fa355 {
+namespace FA355_NS {
 
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO_id O_id in float32, one row per D/8 threads.
@@ -402,4 +402,4 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   if (qrow < N) store_rows<D, T>(dQ + head + (size_t)qrow * D, dqacc, scale, hh);
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

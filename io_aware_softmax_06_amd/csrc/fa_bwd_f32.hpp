@@ -10,7 +10,7 @@
 
 #include "fa_common.hpp"
 
-namespace fa355 {
+namespace FA355_NS {
 
 constexpr int kBwdF32Rows = 32;  // streamed rows per staged tile
 
@@ -176,4 +176,4 @@ __global__ __launch_bounds__(64) void fa_bwd_dq_f32_kernel(
   }
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

@@ -4,7 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace fa355 {
+// The kernels' namespace.  A translation unit that builds the kernels with a
+// different workgroup configuration (the d = 256 instances) names another
+// one, so that the two configurations never share a symbol.
+#ifndef FA355_NS
+#define FA355_NS fa355
+#endif
+
+namespace FA355_NS {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -99,4 +106,4 @@ __device__ __forceinline__ void split_range(int s, int S, int rb, int N, bool ca
   hi = min(visible, ((s + 1) * T / S) * kSplitKeys);
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

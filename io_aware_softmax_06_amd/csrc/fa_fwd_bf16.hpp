@@ -50,7 +50,7 @@
 
 #include "fa_common.hpp"
 
-namespace fa355 {
+namespace FA355_NS {
 
 #ifndef FA355_BF16_WAVES
 #define FA355_BF16_WAVES 8
@@ -60,6 +60,12 @@ namespace fa355 {
 #endif
 #ifndef FA355_BF16_VSTAGES
 #define FA355_BF16_VSTAGES FA355_BF16_STAGES
+#endif
+// Waves of one workgroup per SIMD that the register allocation must allow:
+// 2 for the 8-wave workgroups (two per SIMD); 1 when a 4-wave workgroup
+// fills the LDS alone (d = 256), which leaves it 512 registers per lane.
+#ifndef FA355_BF16_OCCUPANCY
+#define FA355_BF16_OCCUPANCY 2
 #endif
 constexpr int kWaves = FA355_BF16_WAVES;
 constexpr int kThreads = 64 * kWaves;
@@ -362,7 +368,8 @@ __device__ __forceinline__ uint32_t lds_read32(uint32_t lds_addr) {
 }
 
 template <int D, bool CAUSAL, int MODE, typename T = __bf16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(FA355_BF16_OCCUPANCY, FA355_BF16_OCCUPANCY))) void
 fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Lse, int N,
@@ -370,7 +377,7 @@ fa_fwd_bf16_kernel(
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
   using V8 = typename Elem<T>::v8;  // eight 16-bit elements of type T
-  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dimension");
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
   constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)
@@ -855,4 +862,4 @@ fa_fwd_bf16_kernel(
   }
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

@@ -13,23 +13,26 @@
 
 #include "fa_common.hpp"
 
-namespace fa355 {
+namespace FA355_NS {
 
-constexpr int kF32Keys = 32;  // keys per staged tile
+// Keys per staged tile: 32, or 16 at d = 256 (two f32 tiles of 16 KB each).
+template <int D>
+constexpr int kF32Keys = D > 128 ? 16 : 32;
 
 template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ Lse, int N, int BH, int num_qtiles, float scale,
     float scale_log2, ModeArgs split_args) {
-  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dimension");
+  constexpr int kKeys = kF32Keys<D>;
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
   constexpr int kLanesPerRow = D >= 64 ? D / 64 : 1;
   constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
   constexpr int kDl = D / kLanesPerRow;     // components of d held per lane
-  __shared__ f32x4 ks[kF32Keys][D / 4];
-  __shared__ f32x4 vs[kF32Keys][D / 4];
+  __shared__ f32x4 ks[kKeys][D / 4];
+  __shared__ f32x4 vs[kKeys][D / 4];
 
   const int lane = threadIdx.x;
   const int part = lane / kRows;  // which 64 components of d (0 when d = 64)
@@ -64,16 +67,16 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
   int kv_lo = 0, kv_hi = N;
   if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
   const int kv_end = CAUSAL ? min(kv_hi, q0 + kRows) : kv_hi;
-  static_assert(kMaskBlock % kF32Keys == 0 && kMaskBlock % kRows == 0, "mask blocks");
+  static_assert(kMaskBlock % kKeys == 0 && kMaskBlock % kRows == 0, "mask blocks");
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const uint8_t* mrow = nullptr;
   if (SPARSE)
     mrow = split_args.mask +
            ((size_t)mask_head(split_args, bh) * nb + q0 / kMaskBlock) * (size_t)nb;
-  for (int kv0 = kv_lo; kv0 < kv_end; kv0 += kF32Keys) {
+  for (int kv0 = kv_lo; kv0 < kv_end; kv0 += kKeys) {
     if (SPARSE && mrow[kv0 / kMaskBlock] == 0) continue;  // same for the whole workgroup
     __syncthreads();
-    for (int c = lane; c < kF32Keys * (D / 4); c += 64) {
+    for (int c = lane; c < kKeys * (D / 4); c += 64) {
       const int row = c / (D / 4), col = c % (D / 4);
       const int key = kv0 + row;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
@@ -86,10 +89,10 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
     }
     __syncthreads();
 
-    float s[kF32Keys];
+    float s[kKeys];
     float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < kF32Keys; ++j) {
+    for (int j = 0; j < kKeys; ++j) {
       float acc = 0.f;
 #pragma unroll
       for (int t = 0; t < kDl / 4; ++t) {
@@ -99,7 +102,8 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
         acc = __builtin_fmaf(q[t][2], kk[2], acc);
         acc = __builtin_fmaf(q[t][3], kk[3], acc);
       }
-      if (kLanesPerRow == 2) acc += other_half(acc);
+      if (kLanesPerRow >= 2) acc += other_half(acc);
+      if (kLanesPerRow == 4) acc += __shfl_xor(acc, 16, 64);
       const int key = kv0 + j;
       s[j] = (key >= kv_end || (CAUSAL && key > qrow)) ? kNegInf : acc;
       mx = fmaxf(mx, s[j]);
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
 #pragma unroll
     for (int t = 0; t < kDl / 4; ++t) o[t] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kF32Keys; ++j) {
+    for (int j = 0; j < kKeys; ++j) {
       const float p = fast_exp2(__builtin_fmaf(s[j], scale_log2, -base));
       l_run += p;
 #pragma unroll
@@ -148,4 +152,4 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
   }
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

@@ -17,7 +17,7 @@
 
 #include "fa_common.hpp"
 
-namespace fa355 {
+namespace FA355_NS {
 
 constexpr int kMergeThreads = 256;
 
@@ -76,4 +76,4 @@ __global__ __launch_bounds__(kMergeThreads) void fa_merge_kernel(
   }
 }
 
-}  // namespace fa355
+}  // namespace FA355_NS

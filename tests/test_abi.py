@@ -287,3 +287,13 @@ def test_bwd_workspace_checks(lib):
     assert call_bwd(ws=WSB + 64) == fa.FA_ERR_WORKSPACE
     assert call_bwd(ws=GK) == fa.FA_ERR_ALIAS
     assert call_bwd(ws=DO + 256) == fa.FA_ERR_ALIAS
+
+
+
+def test_d256_forward_only(lib):
+    # d = 256 passes the forward checks; the backward and block-sparse paths
+    # take d <= 128 (checked before any HIP call).
+    assert fa.fa_fwd_splitkv_workspace(1, 1, 64, 256, 2) == 2 * 64 * 257 * 4
+    assert call_sparse(d=256) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_bwd(d=256) == fa.FA_ERR_UNSUPPORTED_D
+    assert fa.fa_bwd_workspace(1, 1, 64, 256) == fa.FA_ERR_UNSUPPORTED_D

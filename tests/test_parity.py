@@ -82,6 +82,11 @@ SMALL = [
     (1, 2, 129, 32, "fp16", True),
     (1, 1, 100, 32, "fp32", False),
     (1, 2, 333, 32, "fp32", True),
+    (1, 1, 1, 256, "bf16", False),
+    (1, 2, 300, 256, "bf16", True),
+    (2, 1, 700, 256, "fp16", False),
+    (1, 1, 129, 256, "fp32", True),
+    (1, 2, 77, 256, "fp32", False),
 ]
 
 

@@ -94,6 +94,8 @@ SMALL = [
     (2, 1, 300, 64, "fp16", False, 4),
     (1, 2, 700, 32, "bf16", True, 3),
     (1, 1, 300, 32, "fp32", False, 2),
+    (1, 2, 600, 256, "bf16", True, 3),
+    (1, 1, 200, 256, "fp32", False, 2),
 ]
 
 

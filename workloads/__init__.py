@@ -157,10 +157,10 @@ BWD_CAUSAL_4K = Workload("bwd_causal_bf16_b2h32n4096d128", 2, 32, 4096, 128, "bf
 BY_NAME[BWD_CAUSAL_4K.name] = BWD_CAUSAL_4K
 
 
-# More element types and head dimensions: the causal shape in fp16, and
-# d = 32 at B=4, H=32, N=2048 (the same number of heads times rows as the
-# multi-head workload's twice over).
+# More element types and head dimensions: the causal shape in fp16, d = 32
+# at B=4, H=32, N=2048, and d = 256 at B=2, H=16, N=4096.
 CAUSAL_4K_FP16 = Workload("causal_fp16_b2h32n4096d128", 2, 32, 4096, 128, "fp16", True)
 MHA_D32 = Workload("mha_bf16_b4h32n2048d32", 4, 32, 2048, 32, "bf16", False)
-for _w in (CAUSAL_4K_FP16, MHA_D32):
+MHA_D256 = Workload("mha_bf16_b2h16n4096d256", 2, 16, 4096, 256, "bf16", False)
+for _w in (CAUSAL_4K_FP16, MHA_D32, MHA_D256):
     BY_NAME[_w.name] = _w
