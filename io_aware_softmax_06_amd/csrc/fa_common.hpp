@@ -74,6 +74,7 @@ enum PathMode : int {
   kDense = 0,   // every key (or every key j <= i)
   kSplit = 1,   // one key range per workgroup, partial results (SplitArgs)
   kSparse = 2,  // only the key blocks a block mask enables (below)
+  kPersist = 3, // as kDense, with each workgroup walking a list of query tiles
 };
 
 // Block-sparse attention: key j is visible to query i iff the byte

@@ -23,11 +23,12 @@
 //    that each half-wave holds 8 consecutive keys per 16-key step.
 //  * K and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4, no registers) in a ring of three buffers each,
-//    each tile issued two loop iterations before the one that reads it.  The LDS layouts are cut so that every operand
-//    read of a lane is one base register plus a compile-time offset and no
-//    read has bank conflicts: K is stored in 32-byte column slabs (one per
-//    16-wide step of d), V in 64-byte column slabs (one per 32-wide block of
-//    d).  K rows are read as MFMA A operands with ds_read_b128; V^T operands
+//    each tile issued two loop iterations before the one that reads it.  The
+//    LDS layouts are cut so that every operand read of a lane is one base
+//    register plus a compile-time offset and no read has bank conflicts: K
+//    is stored in 32-byte column slabs (one per 16-wide step of d), V in
+//    64-byte column slabs (one per 32-wide block of d).  K rows are read as
+//    MFMA A operands with ds_read_b128; V^T operands
 //    come from the V slabs through ds_read_b64_tr_b16, whose 16-lane transpose
 //    turns four 8-byte row pieces into one column fragment.
 //  * The softmax VALU work of a tile is split over both MFMA streams of the
@@ -37,6 +38,10 @@
 //    j+2 under the second half of those exponentials, the row sums and the
 //    bf16 conversion.  sched_group_barrier interleaves each pair; the operand
 //    reads are issued a few MFMAs ahead from inline asm.  One barrier per tile.
+//  * Causal launches with more query tiles than CUs are persistent: one
+//    workgroup per CU walks a balanced list of query tiles, and the K/V ring
+//    runs on from one tile to the next, so that the next tile's first K and V
+//    tiles load under the current tile's last iterations.
 //  * The reference point of the online softmax moves only when a row's maximum
 //    grows by more than 2^8 (in base-2 units); until then probabilities are
 //    taken against the stale reference and are at most 2^8, which fp32 and
@@ -80,6 +85,10 @@ static_assert((kStages >= 3 && kVStages == kStages) || (kStages == 3 && kVStages
               "ring depths");
 static_assert(kWaves == 4 || kWaves == 8, "waves per workgroup");
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
+#ifndef FA355_XPHASE
+#define FA355_XPHASE 1
+#endif
+constexpr bool kXPhase = FA355_XPHASE;  // score operands prefetched across the phase boundary
 
 // LDS image of one tile (64 keys x D, bf16):
 //   K: D/16 slabs of [64 rows][32 bytes] (d = 16s .. 16s+15 of every key), the
@@ -240,35 +249,55 @@ struct NoWork {
   __device__ __forceinline__ void operator()(I) const {}
 };
 
-template <int D, typename T = __bf16, int kAheadMax = 6, typename Work = NoWork>
-__device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
-                                           f32x16 (&sacc)[2], Work&& work = Work{}) {
-  using Lay = Bf16Layout<D>;
-  using V8 = typename Elem<T>::v8;
-  constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
-  constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
-  constexpr int kSlots = kAhead + 2;
+// Operand registers of one score tile.  Kept outside score_tile so that the
+// phase before it can issue the first kAhead reads early (the K tile is
+// already valid then): the first MFMAs of the score phase find their operands
+// in registers instead of waiting for LDS.
+template <int D, int kAheadMax = 6>
+struct ScoreOps {
+  static constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
+  static constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
+  static constexpr int kSlots = kAhead + 2;    // a slot is refilled two MFMAs after its use
   u32x4 a[kSlots];
-  auto issue = [&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    a[i % kSlots] = lds_read128<(i / 2) * Lay::kKSlab + (i % 2) * 1024>(kaddr);
-  };
-  static_for<kAhead>(issue);
+  template <int I>
+  __device__ __forceinline__ void issue(uint32_t kaddr) {
+    a[I % kSlots] = lds_read128<(I / 2) * Bf16Layout<D>::kKSlab + (I % 2) * 1024>(kaddr);
+  }
+};
+
+// PRE: the first kAhead reads were issued by the caller (ScoreOps::issue<0..
+// kAhead-1>, in order, with no LDS operation of its own after them).
+template <int D, typename T = __bf16, bool PRE = false, typename Work = NoWork>
+__device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
+                                           f32x16 (&sacc)[2], ScoreOps<D>& ops,
+                                           Work&& work = Work{}) {
+  using V8 = typename Elem<T>::v8;
+  using Ops = ScoreOps<D>;
+  constexpr int kMfmas = Ops::kMfmas, kAhead = Ops::kAhead, kSlots = Ops::kSlots;
+  if constexpr (!PRE)
+    static_for<kAhead>([&](auto ic) { ops.template issue<decltype(ic)::value>(kaddr); });
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
   static_for<kMfmas>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (i + kAhead < kMfmas) {
-      issue(std::integral_constant<int, i + kAhead>{});
+      ops.template issue<i + kAhead>(kaddr);
       lds_wait<kAhead>();
     } else {
       lds_wait<kMfmas - 1 - i>();
     }
-    pin(a[i % kSlots]);
-    sacc[i % 2] = Elem<T>::mfma(__builtin_bit_cast(V8, a[i % kSlots]), qf[i / 2], sacc[i % 2]);
+    pin(ops.a[i % kSlots]);
+    sacc[i % 2] = Elem<T>::mfma(__builtin_bit_cast(V8, ops.a[i % kSlots]), qf[i / 2], sacc[i % 2]);
     work(ic);
     __builtin_amdgcn_sched_barrier(0);
   });
+}
+
+template <int D, typename T = __bf16, typename Work = NoWork>
+__device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
+                                           f32x16 (&sacc)[2], Work&& work = Work{}) {
+  ScoreOps<D> ops;
+  score_tile<D, T, false>(kaddr, qf, sacc, ops, work);
 }
 
 // O^T[db] += V^T[32db.., 16-key step] P^T for the four 16-key steps of a tile.
@@ -276,15 +305,26 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T
 // where the group's d0 = 32db + 16(g%2) and key0 = 16s + 8(g/2) [+ 4 for the
 // second read]; the transpose hands lane i the column d0 + i.  vaddr = LDS
 // address of this lane's piece in slab 0, step 0, first read.
-template <int D, typename T = __bf16, int kAheadMax = 4, typename Work = NoWork>
+// kExtraFrom: from that MFMA on, the caller's work issues one more LDS read
+// after each MFMA (the next score tile's first operands); the waits count them.
+template <int D, typename T = __bf16, int kExtraFrom = 1 << 20, typename Work = NoWork>
 __device__ __forceinline__ void pv_tile(uint32_t vaddr, const typename Elem<T>::v8 (&pf)[kBN / 16],
                                         f32x16 (&oacc)[D / 32], Work&& work = Work{}) {
   using Lay = Bf16Layout<D>;
   using V8 = typename Elem<T>::v8;
+  constexpr int kAheadMax = 4;
   constexpr int kBlocks = D / 32;
   constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
   constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
   constexpr int kSlots = kAhead + 2;            // a slot is refilled two MFMAs after its use
+  // Extra reads issued after the reads of MFMA i (in the chunks i - kAhead ..
+  // i - 1, from kExtraFrom on): they are younger, so a wait for MFMA i's
+  // operands allows that many more outstanding operations.
+  auto extras = [](auto ic) constexpr {
+    constexpr int i = decltype(ic)::value;
+    constexpr int lo = (i - kAhead > kExtraFrom ? i - kAhead : kExtraFrom);
+    return i - lo > 0 ? i - lo : 0;
+  };
   u32x2 v[kSlots][2];
   auto issue = [&](auto ic) {
     constexpr int i = decltype(ic)::value;
@@ -297,11 +337,13 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const typename Elem<T>::
   static_for<kMfmas>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     constexpr int s = i / kBlocks, db = i % kBlocks;
+    constexpr int kX = extras(ic);
+    static_assert(2 * kAhead + kX <= 15, "lgkmcnt holds at most 15");
     if constexpr (i + kAhead < kMfmas) {
       issue(std::integral_constant<int, i + kAhead>{});
-      lds_wait<2 * kAhead>();
+      lds_wait<2 * kAhead + kX>();
     } else {
-      lds_wait<2 * (kMfmas - 1 - i)>();
+      lds_wait<2 * (kMfmas - 1 - i) + kX>();
     }
     u32x2(&cur)[2] = v[i % kSlots];
     pin(cur[0]);
@@ -360,6 +402,37 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nq, int& bh, int& 
   }
 }
 
+// Persistent launches: workgroup b's k-th (batch*head, query tile), or false
+// when it has no k-th.  The workgroups of one XCD (ids congruent mod 8) share
+// that XCD's heads, as in map_tile.  The XCD's tiles are ranked in groups of
+// two heads (one when the XCD holds an odd count), and inside a group level
+// by level, causal levels longest first (non-causal: one head at a time, its
+// tiles in order); round k hands out ranks k*W .. k*W+W-1
+// to the XCD's W workgroups, in reverse order on odd rounds.  Causal tile
+// lengths fall linearly with the level, so the reversal pairs a round's long
+// tiles with the next round's short ones and every workgroup ends up with
+// about the same number of key tiles.
+template <bool CAUSAL>
+__device__ __forceinline__ bool persist_item(int b, int k, int grid, int BH, int nq, int& bh,
+                                             int& qt) {
+  constexpr int kXcds = 8;
+  int xcd = 0, slot = b, W = grid, hp = BH;
+  if (BH % kXcds == 0 && grid % kXcds == 0) {
+    xcd = b % kXcds;
+    slot = b / kXcds;
+    W = grid / kXcds;
+    hp = BH / kXcds;
+  }
+  const int r = k * W + ((k & 1) ? W - 1 - slot : slot);
+  if (r >= hp * nq) return false;
+  const int G = CAUSAL && hp % 2 == 0 ? 2 : 1;
+  const int grp = r / (G * nq), rr = r - grp * (G * nq);
+  const int lev = rr / G;
+  qt = CAUSAL ? nq - 1 - lev : lev;
+  bh = xcd * hp + grp * G + (rr - lev * G);
+  return true;
+}
+
 // 32-bit LDS read from inline asm (see lds_tr16), for the block-sparse tile list.
 __device__ __forceinline__ uint32_t lds_read32(uint32_t lds_addr) {
   uint32_t v;
@@ -376,6 +449,15 @@ fa_fwd_bf16_kernel(
     int BH, int num_qtiles, float scale, float scale_log2, ModeArgs split_args) {
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
+  // Persistent: the grid holds one workgroup per CU and each walks its list
+  // of query tiles (persist_item).  The K/V ring runs on across the tiles:
+  // the refills that would reload past the end of one tile's keys fetch the
+  // next tile's first K and V tiles instead, so that the next prologue finds
+  // them in LDS.  This needs every query tile to stream at least kStages key
+  // tiles (N > (kStages - 1) * kBN, which the host checks): a tile's loop
+  // loads only the next tile's keys, never the one after it.
+  constexpr bool PERSIST = MODE == kPersist;
+  static_assert(!PERSIST || kVStages == kStages, "persistent launches keep K and V in step");
   using V8 = typename Elem<T>::v8;  // eight 16-bit elements of type T
   static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dimension");
   using Lay = Bf16Layout<D>;
@@ -389,7 +471,9 @@ fa_fwd_bf16_kernel(
   const int hh = lane >> 5;  // half-wave
 
   int bh, qt, split = 0;
-  if (SPLIT && CAUSAL) {
+  if constexpr (PERSIST) {
+    if (!persist_item<CAUSAL>(blockIdx.x, 0, gridDim.x, BH, num_qtiles, bh, qt)) return;
+  } else if (SPLIT && CAUSAL) {
     // Longest first: query tiles from the last (most visible keys) down, all
     // key ranges of a tile together (they have equal work); heads fastest, so
     // that consecutive workgroups, which land on different XCDs, keep each
@@ -422,94 +506,7 @@ fa_fwd_bf16_kernel(
   } else {
     map_tile<CAUSAL>(blockIdx.x, BH, num_qtiles, bh, qt);
   }
-  const int q0 = qt * kBM;
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t* Qb = Q + head;
-  const uint16_t* Kb = K + head;
-  const uint16_t* Vb = V + head;
-
-  const int wq0 = q0 + wave * 32;  // first query row of this wave
-  const int qrow = wq0 + qi;
-
-  // Keys of this workgroup: [kv_lo, kv_hi) (the whole row without SPLIT).
-  // Tiles the workgroup streams, and the prefix of them this wave needs.
-  static_assert(kSplitRows % kBM == 0 && kBN == kSplitKeys, "split blocks hold whole tiles");
-  int kv_lo = 0, kv_hi = N;
-  if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
-  const int kv_end = CAUSAL ? min(kv_hi, q0 + kBM) : kv_hi;
-  int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
-  int my_tiles = 0;
-  if (wq0 < N) {
-    const int wave_end = CAUSAL ? min(kv_hi, wq0 + 32) : kv_hi;
-    my_tiles = wave_end > kv_lo ? (wave_end - kv_lo + kBN - 1) / kBN : 0;
-  }
-
-  // Block-sparse: the tile list, built in LDS past the K and V rings.  It
-  // holds, in increasing order, the key blocks that at least one of this
-  // workgroup's 64-row query blocks may see, each as (key block | bits << 24)
-  // with bit r set when query block r of the workgroup sees it.
-  const uint32_t list_off = Lay::kBytes;
-  if constexpr (SPARSE) {
-    constexpr int kQBlocks = kBM / kMaskBlock;
-    static_assert(kBN == kMaskBlock && kBM % kMaskBlock == 0, "mask blocks are tiles");
-    uint32_t* list = reinterpret_cast<uint32_t*>(smem + list_off);
-    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
-    int* counts = reinterpret_cast<int*>(list + nb);
-    const int qb0 = q0 / kMaskBlock;
-    const int kb_end = CAUSAL ? min(nb, qb0 + kQBlocks) : nb;
-    const int qblocks = min(kQBlocks, nb - qb0);
-    const uint8_t* mrow =
-        split_args.mask + ((size_t)mask_head(split_args, bh) * nb + qb0) * (size_t)nb;
-    int total = 0;
-    for (int c = 0; c < kb_end; c += kThreads) {
-      const int kb = c + tid;
-      uint32_t bits = 0;
-      if (kb < kb_end) {
-        for (int r = 0; r < qblocks; ++r)
-          if ((!CAUSAL || kb <= qb0 + r) && mrow[(size_t)r * nb + kb] != 0) bits |= 1u << r;
-      }
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
-      if (lane == 0) counts[wave] = __builtin_popcountll(bal);
-      __syncthreads();
-      int before = total, all = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int cw = counts[w];
-        before += w < wave ? cw : 0;
-        all += cw;
-      }
-      if (bits != 0)
-        list[before + __builtin_popcountll(bal & ((1ull << lane) - 1))] = (uint32_t)kb | (bits << 24);
-      total += all;
-      __syncthreads();
-    }
-    n_tiles = total;
-    my_tiles = wq0 < N ? total : 0;
-  }
-  const int last = n_tiles - 1;
-
-  // Q^T as the B operand of S^T = K Q^T: lane holds d = 16s + 8hh + (0..7).
-  V8 qf[D / 16];
-  {
-    const int qr = min(qrow, N - 1);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[s] = __builtin_bit_cast(
-          V8, *reinterpret_cast<const u32x4*>(Qb + (size_t)qr * D + 16 * s + 8 * hh));
-  }
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  // Running state of this lane's query row: base_run is the base-2 reference
-  // (a rounded product m_ref * scale_log2, kept as that rounded value so that
-  // exp2(base_old - base_new) moves the reference exactly); m_ref is the raw
-  // score it came from.  -FLT_MAX marks "no visible key yet".
-  float base_run = -__FLT_MAX__;
-  float m_ref = kNegInf;
-  float l_run = 0.f;  // this half-wave's part of the denominator
-
-  // Per-lane operand offsets (constant over the loop).
+  // Per-lane operand offsets (constant over the kernel).
   const int arow = key_of_row(qi);
   const int k_lane = arow * 32 + 16 * (hh ^ ((arow >> 3) & 1));
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -523,342 +520,492 @@ fa_fwd_bf16_kernel(
     k_off[r] = tile_lane_offset<D, false>(wave, lane, r);
     v_off[r] = tile_lane_offset<D, true>(wave, lane, r);
   }
-  const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(Kb, N * D * 2);
-  const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(Vb, N * D * 2);
-  // Tile t of the workgroup as an entry: its key block, plus (block-sparse
-  // path) which query blocks see it.  Dense and split paths: key block
-  // kv_lo / kBN + t; block-sparse: the t-th list entry, read from LDS with
-  // asm (callers wait with lds_wait<0> and pin the result).  Entries past the
-  // last tile repeat it: the ring's final refills reload the last tile.
-  auto entry = [&](int tile) -> uint32_t {
-    const int t = min(tile, last);
-    if constexpr (SPARSE) return lds_read32(smem_lds + list_off + 4 * t);
-    else return (uint32_t)(kv_lo / kBN + t);
-  };
-  // Orders uses of an entry after the lds_wait, and moves it to a scalar
-  // register (it is the same in every lane).
-  auto pin_entry = [](uint32_t& e) {
-    asm volatile("" : "+v"(e));
-    e = __builtin_amdgcn_readfirstlane(e);
-  };
-  auto entry_kv0 = [](uint32_t e) { return (int)(SPARSE ? e & 0xFFFFFFu : e) * kBN; };
-  // Does this wave's 64-row query block see the tile at all?
-  auto entry_seen = [&](uint32_t e) { return !SPARSE || ((e >> (24 + (wave >> 1))) & 1u) != 0; };
-  auto load_k = [&](int slot, uint32_t e) {
-    load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes, k_rsrc, entry_kv0(e), wave,
-                        k_off);
-  };
-  auto load_v = [&](int slot, uint32_t e) {
-    load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes, v_rsrc, entry_kv0(e), wave,
-                        v_off);
-  };
 
-  // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
-  // maximum, reference update, the exponentials of block 0 and their sum.
-  // Stage 2: the exponentials of block 1, the row sum into l_run, and P^T as
-  // bf16 B operands of O^T += V^T P^T (16-key step s2 takes elements
-  // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
-  // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
-  auto mask_tile = [&](uint32_t ent, f32x16(&sc)[2]) {
-    const int kv0 = entry_kv0(ent);
-    const bool hidden = !entry_seen(ent);  // a key block this wave's query block does not see
-    const bool need_mask = hidden || (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
-    if (need_mask) {
+  // K/V ring slot of the current query tile's first key tile (persistent
+  // launches carry the ring position over from tile to tile).
+  int ring = 0;
+  V8 qf[D / 16];  // Q^T as the B operand of S^T = K Q^T: lane holds d = 16s + 8hh + (0..7)
+  auto load_q = [&](int bh_q, int qt_q) {
+    const int qr = min(qt_q * kBM + wave * 32 + qi, N - 1);
+    const uint16_t* qp = Q + (size_t)bh_q * N * D + (size_t)qr * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(qp + 16 * s));
+  };
+  load_q(bh, qt);
+  for (int nth = 0;; ++nth) {
+    bool has_next = false;  // persistent: this workgroup has a next query tile (nbh, nqt)
+    int nbh = 0, nqt = 0;
+    if constexpr (PERSIST)
+      has_next = persist_item<CAUSAL>(blockIdx.x, nth + 1, gridDim.x, BH, num_qtiles, nbh, nqt);
+    const int q0 = qt * kBM;
+    const size_t head = (size_t)bh * N * D;
+    const uint16_t* Kb = K + head;
+    const uint16_t* Vb = V + head;
+
+    const int wq0 = q0 + wave * 32;  // first query row of this wave
+    const int qrow = wq0 + qi;
+
+    // Keys of this workgroup: [kv_lo, kv_hi) (the whole row without SPLIT).
+    // Tiles the workgroup streams, and the prefix of them this wave needs.
+    static_assert(kSplitRows % kBM == 0 && kBN == kSplitKeys, "split blocks hold whole tiles");
+    int kv_lo = 0, kv_hi = N;
+    if (SPLIT) split_range(split, split_args.num_splits, q0 / kSplitRows, N, CAUSAL, kv_lo, kv_hi);
+    const int kv_end = CAUSAL ? min(kv_hi, q0 + kBM) : kv_hi;
+    int n_tiles = kv_end > kv_lo ? (kv_end - kv_lo + kBN - 1) / kBN : 0;
+    int my_tiles = 0;
+    if (wq0 < N) {
+      const int wave_end = CAUSAL ? min(kv_hi, wq0 + 32) : kv_hi;
+      my_tiles = wave_end > kv_lo ? (wave_end - kv_lo + kBN - 1) / kBN : 0;
+    }
+
+    // Block-sparse: the tile list, built in LDS past the K and V rings.  It
+    // holds, in increasing order, the key blocks that at least one of this
+    // workgroup's 64-row query blocks may see, each as (key block | bits << 24)
+    // with bit r set when query block r of the workgroup sees it.
+    const uint32_t list_off = Lay::kBytes;
+    if constexpr (SPARSE) {
+      constexpr int kQBlocks = kBM / kMaskBlock;
+      static_assert(kBN == kMaskBlock && kBM % kMaskBlock == 0, "mask blocks are tiles");
+      uint32_t* list = reinterpret_cast<uint32_t*>(smem + list_off);
+      const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+      int* counts = reinterpret_cast<int*>(list + nb);
+      const int qb0 = q0 / kMaskBlock;
+      const int kb_end = CAUSAL ? min(nb, qb0 + kQBlocks) : nb;
+      const int qblocks = min(kQBlocks, nb - qb0);
+      const uint8_t* mrow =
+          split_args.mask + ((size_t)mask_head(split_args, bh) * nb + qb0) * (size_t)nb;
+      int total = 0;
+      for (int c = 0; c < kb_end; c += kThreads) {
+        const int kb = c + tid;
+        uint32_t bits = 0;
+        if (kb < kb_end) {
+          for (int r = 0; r < qblocks; ++r)
+            if ((!CAUSAL || kb <= qb0 + r) && mrow[(size_t)r * nb + kb] != 0) bits |= 1u << r;
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+        if (lane == 0) counts[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        int before = total, all = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const int cw = counts[w];
+          before += w < wave ? cw : 0;
+          all += cw;
+        }
+        if (bits != 0)
+          list[before + __builtin_popcountll(bal & ((1ull << lane) - 1))] =
+              (uint32_t)kb | (bits << 24);
+        total += all;
+        __syncthreads();
+      }
+      n_tiles = total;
+      my_tiles = wq0 < N ? total : 0;
+    }
+    const int last = n_tiles - 1;
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+    // Running state of this lane's query row: base_run is the base-2 reference
+    // (a rounded product m_ref * scale_log2, kept as that rounded value so that
+    // exp2(base_old - base_new) moves the reference exactly); m_ref is the raw
+    // score it came from.  -FLT_MAX marks "no visible key yet".
+    float base_run = -__FLT_MAX__;
+    float m_ref = kNegInf;
+    float l_run = 0.f;  // this half-wave's part of the denominator
+
+    const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(Kb, N * D * 2);
+    const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(Vb, N * D * 2);
+    const size_t next_head = (size_t)nbh * N * D;
+    const __amdgpu_buffer_rsrc_t k_rsrc_next = head_resource(K + next_head, N * D * 2);
+    const __amdgpu_buffer_rsrc_t v_rsrc_next = head_resource(V + next_head, N * D * 2);
+    constexpr uint32_t kNextTile = 1u << 31;  // entry flag: a key tile of the next query tile
+    // Tile t of the workgroup as an entry: its key block, plus (block-sparse
+    // path) which query blocks see it.  Dense and split paths: key block
+    // kv_lo / kBN + t; block-sparse: the t-th list entry, read from LDS with
+    // asm (callers wait with lds_wait<0> and pin the result).  Entries past the
+    // last tile repeat it (the ring's final refills reload the last tile), or,
+    // persistent with a next query tile, stand for that tile's key tiles.
+    auto entry = [&](int tile) -> uint32_t {
+      if constexpr (PERSIST) {
+        if (has_next && tile > last) return (uint32_t)(tile - n_tiles) | kNextTile;
+      }
+      const int t = min(tile, last);
+      if constexpr (SPARSE) return lds_read32(smem_lds + list_off + 4 * t);
+      else return (uint32_t)(kv_lo / kBN + t);
+    };
+    // Orders uses of an entry after the lds_wait, and moves it to a scalar
+    // register (it is the same in every lane).
+    auto pin_entry = [](uint32_t& e) {
+      asm volatile("" : "+v"(e));
+      e = __builtin_amdgcn_readfirstlane(e);
+    };
+    auto entry_kv0 = [](uint32_t e) {
+      return (int)(SPARSE ? e & 0xFFFFFFu : PERSIST ? e & ~kNextTile : e) * kBN;
+    };
+    // Does this wave's 64-row query block see the tile at all?
+    auto entry_seen = [&](uint32_t e) { return !SPARSE || ((e >> (24 + (wave >> 1))) & 1u) != 0; };
+    auto load_k = [&](int slot, uint32_t e) {
+      load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes,
+                          PERSIST && (e & kNextTile) ? k_rsrc_next : k_rsrc, entry_kv0(e), wave,
+                          k_off);
+    };
+    auto load_v = [&](int slot, uint32_t e) {
+      load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes,
+                          PERSIST && (e & kNextTile) ? v_rsrc_next : v_rsrc, entry_kv0(e), wave,
+                          v_off);
+    };
+
+    // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
+    // maximum, reference update, the exponentials of block 0 and their sum.
+    // Stage 2: the exponentials of block 1, the row sum into l_run, and P^T as
+    // bf16 B operands of O^T += V^T P^T (16-key step s2 takes elements
+    // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
+    // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
+    auto mask_tile = [&](uint32_t ent, f32x16(&sc)[2]) {
+      const int kv0 = entry_kv0(ent);
+      const bool hidden = !entry_seen(ent);  // a key block this wave's query block does not see
+      const bool need_mask = hidden || (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
+            if (hidden || key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
+          }
+      }
+    };
+    // The softmax of a tile as numbered steps, so that each MFMA of a phase can
+    // be given its share (step s of NS goes after MFMA s * kMf / NS).
+    // Stage 1 (18 steps): the row maximum as a chain of three-input maxima
+    // (two per step), the half-wave exchange and reference update, eight pairs
+    // of exponentials of block 0, their sum.
+    // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
+    // into l_run, eight pairs of bf16 conversions into the P^T operands.  The
+    // sums are taken over the float32 probabilities: summing their bf16
+    // roundings instead would move L by up to 2^-9 on rows with few keys.
+    struct SoftmaxState {
+      float m, alpha, half_sum;
+      bool need;
+    };
+    constexpr int kStage1Steps = 18, kStage2Steps = 17;
+    auto stage1_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st) {
+      constexpr int sidx = decltype(sic)::value;
+      if constexpr (sidx < 8) {
+        constexpr int kb = sidx >> 2, e = 4 * (sidx & 3);
+        if constexpr (sidx == 0) st.m = fmaxf(sc[0][0], sc[0][1]);
+        else st.m = fmaxf(fmaxf(st.m, sc[kb][e]), sc[kb][e + 1]);
+        st.m = fmaxf(fmaxf(st.m, sc[kb][e + 2]), sc[kb][e + 3]);
+      } else if constexpr (sidx == 8) {
+        const float mx = max_halves(st.m);
+        const float cand = mx * scale_log2;  // -inf for a fully masked tile
+        st.need = cand > base_run + kTau;
+        const float base_new = st.need ? cand : base_run;
+        st.alpha = fast_exp2(base_run - base_new);
+        m_ref = st.need ? mx : m_ref;
+        base_run = base_new;
+      } else if constexpr (sidx < 17) {
+        constexpr int e = 2 * (sidx - 9);
+        sc[0][e] = fast_exp2(__builtin_fmaf(sc[0][e], scale_log2, -base_run));
+        sc[0][e + 1] = fast_exp2(__builtin_fmaf(sc[0][e + 1], scale_log2, -base_run));
+      } else {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = sc[0][2 * i] + sc[0][2 * i + 1];
+        st.half_sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      }
+    };
+    auto stage2_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
+      constexpr int sidx = decltype(sic)::value;
+      if constexpr (sidx < 8) {
+        constexpr int e = 2 * sidx;
+        sc[1][e] = fast_exp2(__builtin_fmaf(sc[1][e], scale_log2, -base_run));
+        sc[1][e + 1] = fast_exp2(__builtin_fmaf(sc[1][e + 1], scale_log2, -base_run));
+      } else if constexpr (sidx == 8) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = sc[1][2 * i] + sc[1][2 * i + 1];
+        const float lsum =
+            st.half_sum + (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+        l_run = __builtin_fmaf(l_run, st.alpha, lsum);
+      } else {
+        // pair k of the 32 conversions: elements 4k .. 4k+3 of the tile's keys
+        constexpr int k = sidx - 9;
+        constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (T)sc[s2 >> 1][8 * (s2 & 1) + j];
+      }
+    };
+    // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
+    auto run_steps = [&](auto ic, auto nsteps_ic, auto&& step) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int NS = decltype(nsteps_ic)::value;
+      static_for<NS>([&](auto sic) {
+        constexpr int sidx = decltype(sic)::value;
+        if constexpr (sidx * kMf / NS == i) step(sic);
+      });
+    };
+    auto stage1 = [&](f32x16(&sc)[2], SoftmaxState& st) {
+      static_for<kStage1Steps>([&](auto sic) { stage1_step(sic, sc, st); });
+    };
+    auto stage2 = [&](f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
+      static_for<kStage2Steps>([&](auto sic) { stage2_step(sic, sc, st, pfo); });
+    };
+    // Empty asm that ties values to this point of the program: the compiler
+    // would otherwise sink them past the next branch, next to their use.
+    auto pin_scores = [&](f32x16(&sc)[2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
-          if (hidden || key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
+        for (int q = 0; q < 4; ++q) {
+          u32x4 w = {__float_as_uint(sc[kb][4 * q]), __float_as_uint(sc[kb][4 * q + 1]),
+                     __float_as_uint(sc[kb][4 * q + 2]), __float_as_uint(sc[kb][4 * q + 3])};
+          pin(w);
+          sc[kb][4 * q] = __uint_as_float(w[0]);
+          sc[kb][4 * q + 1] = __uint_as_float(w[1]);
+          sc[kb][4 * q + 2] = __uint_as_float(w[2]);
+          sc[kb][4 * q + 3] = __uint_as_float(w[3]);
         }
-    }
-  };
-  // The softmax of a tile as numbered steps, so that each MFMA of a phase can
-  // be given its share (step s of NS goes after MFMA s * kMf / NS).
-  // Stage 1 (18 steps): the row maximum as a chain of three-input maxima
-  // (two per step), the half-wave exchange and reference update, eight pairs
-  // of exponentials of block 0, their sum.
-  // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
-  // into l_run, eight pairs of bf16 conversions into the P^T operands.  The
-  // sums are taken over the float32 probabilities: summing their bf16
-  // roundings instead would move L by up to 2^-9 on rows with few keys.
-  struct SoftmaxState {
-    float m, alpha, half_sum;
-    bool need;
-  };
-  constexpr int kStage1Steps = 18, kStage2Steps = 17;
-  auto stage1_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st) {
-    constexpr int sidx = decltype(sic)::value;
-    if constexpr (sidx < 8) {
-      constexpr int kb = sidx >> 2, e = 4 * (sidx & 3);
-      if constexpr (sidx == 0) st.m = fmaxf(sc[0][0], sc[0][1]);
-      else st.m = fmaxf(fmaxf(st.m, sc[kb][e]), sc[kb][e + 1]);
-      st.m = fmaxf(fmaxf(st.m, sc[kb][e + 2]), sc[kb][e + 3]);
-    } else if constexpr (sidx == 8) {
-      const float mx = max_halves(st.m);
-      const float cand = mx * scale_log2;  // -inf for a fully masked tile
-      st.need = cand > base_run + kTau;
-      const float base_new = st.need ? cand : base_run;
-      st.alpha = fast_exp2(base_run - base_new);
-      m_ref = st.need ? mx : m_ref;
-      base_run = base_new;
-    } else if constexpr (sidx < 17) {
-      constexpr int e = 2 * (sidx - 9);
-      sc[0][e] = fast_exp2(__builtin_fmaf(sc[0][e], scale_log2, -base_run));
-      sc[0][e + 1] = fast_exp2(__builtin_fmaf(sc[0][e + 1], scale_log2, -base_run));
-    } else {
-      float q[8];
+    };
+    auto pin_probs = [&](V8(&pfo)[kBN / 16]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = sc[0][2 * i] + sc[0][2 * i + 1];
-      st.half_sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-    }
-  };
-  auto stage2_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
-    constexpr int sidx = decltype(sic)::value;
-    if constexpr (sidx < 8) {
-      constexpr int e = 2 * sidx;
-      sc[1][e] = fast_exp2(__builtin_fmaf(sc[1][e], scale_log2, -base_run));
-      sc[1][e + 1] = fast_exp2(__builtin_fmaf(sc[1][e + 1], scale_log2, -base_run));
-    } else if constexpr (sidx == 8) {
-      float q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = sc[1][2 * i] + sc[1][2 * i + 1];
-      const float lsum =
-          st.half_sum + (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
-      l_run = __builtin_fmaf(l_run, st.alpha, lsum);
-    } else {
-      // pair k of the 32 conversions: elements 4k .. 4k+3 of the tile's keys
-      constexpr int k = sidx - 9;
-      constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
-#pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (T)sc[s2 >> 1][8 * (s2 & 1) + j];
-    }
-  };
-  // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
-  auto run_steps = [&](auto ic, auto nsteps_ic, auto&& step) {
-    constexpr int i = decltype(ic)::value;
-    constexpr int NS = decltype(nsteps_ic)::value;
-    static_for<NS>([&](auto sic) {
-      constexpr int sidx = decltype(sic)::value;
-      if constexpr (sidx * kMf / NS == i) step(sic);
-    });
-  };
-  auto stage1 = [&](f32x16(&sc)[2], SoftmaxState& st) {
-    static_for<kStage1Steps>([&](auto sic) { stage1_step(sic, sc, st); });
-  };
-  auto stage2 = [&](f32x16(&sc)[2], SoftmaxState& st, V8(&pfo)[kBN / 16]) {
-    static_for<kStage2Steps>([&](auto sic) { stage2_step(sic, sc, st, pfo); });
-  };
-  // Empty asm that ties values to this point of the program: the compiler
-  // would otherwise sink them past the next branch, next to their use.
-  auto pin_scores = [&](f32x16(&sc)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 w = {__float_as_uint(sc[kb][4 * q]), __float_as_uint(sc[kb][4 * q + 1]),
-                   __float_as_uint(sc[kb][4 * q + 2]), __float_as_uint(sc[kb][4 * q + 3])};
+      for (int s2 = 0; s2 < kBN / 16; ++s2) {
+        u32x4 w = __builtin_bit_cast(u32x4, pfo[s2]);
         pin(w);
-        sc[kb][4 * q] = __uint_as_float(w[0]);
-        sc[kb][4 * q + 1] = __uint_as_float(w[1]);
-        sc[kb][4 * q + 2] = __uint_as_float(w[2]);
-        sc[kb][4 * q + 3] = __uint_as_float(w[3]);
+        pfo[s2] = __builtin_bit_cast(V8, w);
       }
-  };
-  auto pin_probs = [&](V8(&pfo)[kBN / 16]) {
-#pragma unroll
-    for (int s2 = 0; s2 < kBN / 16; ++s2) {
-      u32x4 w = __builtin_bit_cast(u32x4, pfo[s2]);
-      pin(w);
-      pfo[s2] = __builtin_bit_cast(V8, w);
-    }
-    asm volatile("" : "+v"(l_run));
-  };
+      asm volatile("" : "+v"(l_run));
+    };
 
-  // A workgroup whose key range is empty (a split past the causal diagonal)
-  // skips straight to the epilogue, which then writes L = -inf and O = 0.
-  if (n_tiles > 0) {
-    // Prologue.  Ring slots: K tile j lives in slot j % kStages, V tile j in
-    // slot j % kVStages.  Iteration t reads V_t and K_{t+2}.  It refills the
-    // slot of K_{t+1} (read in iteration t-1) with K_{t+1+kStages}, and the
-    // V slot freed by iteration t-1 with V_{t-1+kVStages}.  Before iteration
-    // 0, K_0..K_2 and V_0 must have landed.  With equal ring depths S, the
-    // loads of the "iterations" 2-S .. -1 are issued here in loop order so
-    // that the vmcnt at the end of every iteration stays exact.  K_S goes to
-    // the slot of K_0, which the prologue's scores read, so it waits for the
-    // second barrier.
-    uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);
-    if constexpr (SPARSE) {
-      lds_wait<0>();
-      pin_entry(e0);
-      pin_entry(e1);
-      pin_entry(e2);
-    }
-    load_k(0, e0);
-    load_k(1, e1);
-    load_k(2, e2);
-    load_v(0, e0);
-    if constexpr (kVStages == kStages) {
-#pragma unroll
-      for (int j = 3; j < kStages; ++j) {
-        uint32_t ej = entry(j), ev = entry(j - 2);
+    // A workgroup whose key range is empty (a split past the causal diagonal)
+    // skips straight to the epilogue, which then writes L = -inf and O = 0.
+    // Persistent tiles always stream keys.
+    if (PERSIST || n_tiles > 0) {
+      // Prologue.  Ring slots: K tile j lives in slot j % kStages, V tile j in
+      // slot j % kVStages.  Iteration t reads V_t and K_{t+2}.  It refills the
+      // slot of K_{t+1} (read in iteration t-1) with K_{t+1+kStages}, and the
+      // V slot freed by iteration t-1 with V_{t-1+kVStages}.  Before iteration
+      // 0, K_0..K_2 and V_0 must have landed.  With equal ring depths S, the
+      // loads of the "iterations" 2-S .. -1 are issued here in loop order so
+      // that the vmcnt at the end of every iteration stays exact.  K_S goes to
+      // the slot of K_0, which the prologue's scores read, so it waits for the
+      // second barrier.
+      //
+      // Persistent launches: tile j of the current query tile is in slot
+      // (ring + j) % kStages, and the tails of the previous query tile's loop
+      // have already loaded (and waited for) this prologue's tiles.
+      auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
+      uint32_t e0 = entry(0);
+      if (!PERSIST || nth == 0) {
+        uint32_t e1 = entry(1), e2 = entry(2);
         if constexpr (SPARSE) {
           lds_wait<0>();
-          pin_entry(ej);
-          pin_entry(ev);
+          pin_entry(e0);
+          pin_entry(e1);
+          pin_entry(e2);
         }
-        load_k(j, ej);
-        load_v(j - 2, ev);
+        load_k(0, e0);
+        load_k(1, e1);
+        load_k(2, e2);
+        load_v(0, e0);
+        if constexpr (kVStages == kStages) {
+#pragma unroll
+          for (int j = 3; j < kStages; ++j) {
+            uint32_t ej = entry(j), ev = entry(j - 2);
+            if constexpr (SPARSE) {
+              lds_wait<0>();
+              pin_entry(ej);
+              pin_entry(ev);
+            }
+            load_k(j, ej);
+            load_v(j - 2, ev);
+          }
+          uint32_t ev = entry(kStages - 2);
+          if constexpr (SPARSE) {
+            lds_wait<0>();
+            pin_entry(ev);
+          }
+          load_v(kStages - 2, ev);
+          wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
+        } else {
+          wait_vmcnt<0>();  // a 2-deep V ring: iteration 0 loads V_1
+        }
+        block_sync();
       }
-      uint32_t ev = entry(kStages - 2);
-      if constexpr (SPARSE) {
-        lds_wait<0>();
-        pin_entry(ev);
-      }
-      load_v(kStages - 2, ev);
-      wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();  // K_0..K_2 and V_0 have landed
-    } else {
-      wait_vmcnt<0>();  // a 2-deep V ring: iteration 0 loads V_1
-    }
-    block_sync();
 
-    f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
-    V8 pf[kBN / 16];  // P^T of the tile whose P V is next
-    if (my_tiles > 0) {
-      score_tile<D, T>(k_addr(0), qf, sA);
-      score_tile<D, T>(k_addr(1), qf, sB);
-      mask_tile(e0, sA);
-      SoftmaxState st;
-      stage1(sA, st);
-      stage2(sA, st, pf);
-    }
-    uint32_t es = entry(kStages);
-    if constexpr (SPARSE) {
-      lds_wait<0>();
-      pin_entry(es);
-    }
-    block_sync();  // every wave is done reading K_0 before its slot is refilled
-    load_k(0, es);
-
-    // One tile.  On entry pf holds P_t and cur the raw scores of tile t+1;
-    // nxt receives tile t+2.  sk = t % kStages is the K ring position (K_{t+2}
-    // is in slot (sk+2) % kStages); svs = t % kVStages is V_t's slot.
-    auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
-    // The loads of later tiles are issued inside the two MFMA phases rather
-    // than all at the top: eight waves issuing them at once right after the
-    // barrier queue up in the address unit.  With a 2-deep V ring the V load
-    // goes first, so that it has the whole iteration to land.
-    constexpr bool kShortV = kVStages == 2;
-    auto refill_v = [&](int sk, int svs, uint32_t ev) {
-      if constexpr (kShortV) load_v(svs ^ 1, ev);
-      else load_v(wrap(sk + kStages - 1), ev);
-    };
-    auto iteration = [&](int t, int sk, int svs, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-      // Entries of this iteration: tile t+1 (masked now), the K tile
-      // t+1+kStages and the V tile (t+1 or t-1+kStages) loaded now.  On the
-      // block-sparse path they are read here, before any operand read of the
-      // iteration is in flight.
-      uint32_t e_next = entry(t + 1), e_k = entry(t + 1 + kStages);
-      uint32_t e_v = kShortV ? e_next : entry(t - 1 + kStages);
-      if constexpr (SPARSE) {
-        lds_wait<0>();
-        pin_entry(e_next);
-        pin_entry(e_k);
-        pin_entry(e_v);
+      f32x16 sA[2], sB[2];  // raw scores / probabilities of two consecutive tiles
+      V8 pf[kBN / 16];  // P^T of the tile whose P V is next
+      // Q has landed here on every path, also in waves with no rows (which
+      // never read it): otherwise the compiler keeps the load pending and
+      // waits for every load in flight before the next Q load reuses qf.
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
+        pin(w);
+        qf[s] = __builtin_bit_cast(V8, w);
       }
-      if (t + 1 < my_tiles) {
-        mask_tile(e_next, cur);
-        // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
-        // the K load of a later tile in the middle.
+      if (my_tiles > 0) {
+        score_tile<D, T>(k_addr(ring), qf, sA);
+        score_tile<D, T>(k_addr(wrap(ring + 1)), qf, sB);
+        mask_tile(e0, sA);
         SoftmaxState st;
-        pv_tile<D, T>(v_addr(svs), pf, oacc, [&](auto ic) {
-          run_steps(ic, std::integral_constant<int, kStage1Steps>{},
-                    [&](auto sic) { stage1_step(sic, cur, st); });
-          if constexpr (kShortV && decltype(ic)::value == 0) refill_v(sk, svs, e_v);
-          if constexpr (decltype(ic)::value == kMf / 2) load_k(wrap(sk + 1), e_k);
-        });
-        pin_scores(cur);
-        asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
-
-        // Phase 2: move the output to the new reference (rare).
-        if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
-#pragma unroll
-          for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
-        }
-
-        // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
-        // with the V load of a later tile in the middle.
-        score_tile<D, T>(k_addr(wrap(sk + 2)), qf, nxt, [&](auto ic) {
-          run_steps(ic, std::integral_constant<int, kStage2Steps>{},
-                    [&](auto sic) { stage2_step(sic, cur, st, pf); });
-          if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(sk, svs, e_v);
-        });
-        pin_probs(pf);
-      } else {
-        if constexpr (kShortV) refill_v(sk, svs, e_v);
-        load_k(wrap(sk + 1), e_k);
-        if (t < my_tiles) pv_tile<D, T>(v_addr(svs), pf, oacc);
-        if constexpr (!kShortV) refill_v(sk, svs, e_v);
+        stage1(sA, st);
+        stage2(sA, st, pf);
       }
+      uint32_t es = entry(kStages);
+      if constexpr (SPARSE) {
+        lds_wait<0>();
+        pin_entry(es);
+      }
+      block_sync();  // every wave is done reading K_0 before its slot is refilled
+      load_k(ring, es);
 
-      // K_{t+3} and V_{t+1} must have landed for every wave before anyone
-      // reads them.  Equal rings: both were issued in iteration t+2-S, and the
-      // loads of the S-2 later iterations may stay in flight.  2-deep V ring:
-      // V_{t+1} was this iteration's first load; only its K load may stay.
-      if constexpr (kShortV) wait_vmcnt<kVmPerTile>();
-      else wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
-      block_sync();
-    };
-
-    // Two tiles per trip so that the two score buffers swap roles instead of
-    // being copied (and, with a 2-deep V ring, V slots are constants).
-    int t = 0, sk = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-      iteration(t, sk, kShortV ? 0 : sk, sB, sA);
-      iteration(t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
-      sk = wrap(sk + 2);
-    }
-    if (t < n_tiles) iteration(t, sk, kShortV ? 0 : sk, sB, sA);
-    // The ring's last refills (clamped repeats of the last tile) are still in
-    // flight; let them land before the workgroup can end and its LDS be reused.
-    wait_vmcnt<0>();
-  }
-
-  // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
-  const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // l_tot = sum_j exp2(s_j c - base_run) with base_run = m_ref c - r, where r
-  // (exact, from one FMA) is the rounding residual of base_run; hence
-  // ln sum_j exp(scale s_j) = m_ref scale + ln l_tot - r ln 2.
-  const float lse = l_tot > 0.f ? __builtin_fmaf(m_ref, scale, logf(l_tot) - __builtin_fmaf(m_ref, scale_log2, -base_run) * kLn2) : kNegInf;
-  if (qrow < N) {
-    if (SPLIT) {
-      const size_t prow = ((size_t)split * BH + bh) * N + qrow;
-      float* orow = split_args.opart + prow * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 o4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][4 * g + r] * inv;
-          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) = o4;
+      // One tile.  On entry pf holds P_t and cur the raw scores of tile t+1;
+      // nxt receives tile t+2.  sk = t % kStages is the K ring position (K_{t+2}
+      // is in slot (sk+2) % kStages); svs = t % kVStages is V_t's slot.
+      // The loads of later tiles are issued inside the two MFMA phases rather
+      // than all at the top: eight waves issuing them at once right after the
+      // barrier queue up in the address unit.  With a 2-deep V ring the V load
+      // goes first, so that it has the whole iteration to land.
+      constexpr bool kShortV = kVStages == 2;
+      auto refill_v = [&](int sk, int svs, uint32_t ev) {
+        if constexpr (kShortV) load_v(svs ^ 1, ev);
+        else load_v(wrap(sk + kStages - 1), ev);
+      };
+      auto iteration = [&](int t, int sk, int svs, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+        // Entries of this iteration: tile t+1 (masked now), the K tile
+        // t+1+kStages and the V tile (t+1 or t-1+kStages) loaded now.  On the
+        // block-sparse path they are read here, before any operand read of the
+        // iteration is in flight.
+        const bool boundary = PERSIST && has_next && t == last;
+        uint32_t e_next = entry(t + 1), e_k = entry(t + 1 + kStages);
+        uint32_t e_v = kShortV ? e_next : entry(t - 1 + kStages);
+        if constexpr (SPARSE) {
+          lds_wait<0>();
+          pin_entry(e_next);
+          pin_entry(e_k);
+          pin_entry(e_v);
         }
-      if (hh == 0) split_args.lpart[prow] = lse;
-    } else {
-      uint16_t* orow = O + head + (size_t)qrow * D;
+        if (t + 1 < my_tiles) {
+          mask_tile(e_next, cur);
+          // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
+          // the K load of a later tile in the middle.
+          SoftmaxState st;
+          // The last MFMAs of this phase issue the first operand reads of the
+          // score phase (K_{t+2} has been valid since the last barrier).
+          ScoreOps<D> sops;
+          const uint32_t k_next = k_addr(wrap(sk + 2));
+          constexpr int kPre = kXPhase ? ScoreOps<D>::kAhead : 0;
+          pv_tile<D, T, kMf - kPre>(v_addr(svs), pf, oacc, [&](auto ic) {
+            constexpr int c = decltype(ic)::value;
+            run_steps(ic, std::integral_constant<int, kStage1Steps>{},
+                      [&](auto sic) { stage1_step(sic, cur, st); });
+            if constexpr (kShortV && c == 0) refill_v(sk, svs, e_v);
+            if constexpr (c == kMf / 2) load_k(wrap(sk + 1), e_k);
+            if constexpr (kPre > 0 && c >= kMf - kPre)
+              sops.template issue<c - (kMf - kPre)>(k_next);
+          });
+          pin_scores(cur);
+          asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
+
+          // Phase 2: move the output to the new reference (rare).
+          if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          T o4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = (T)(oacc[db][4 * g + r] * inv);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
-              __builtin_bit_cast(u32x2, o4);
+            for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
+          }
+
+          // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
+          // with the V load of a later tile in the middle.
+          score_tile<D, T, kXPhase>(k_next, qf, nxt, sops, [&](auto ic) {
+            run_steps(ic, std::integral_constant<int, kStage2Steps>{},
+                      [&](auto sic) { stage2_step(sic, cur, st, pf); });
+            if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(sk, svs, e_v);
+          });
+          pin_probs(pf);
+        } else {
+          if constexpr (kShortV) refill_v(sk, svs, e_v);
+          // Persistent, last tile with a next query tile: K_{t+1+S} is that
+          // tile's K_S, and its slot still holds the next tile's K_0, unread.
+          // The next prologue issues it after its first scores, as every
+          // prologue does.
+          if (!(PERSIST && boundary)) load_k(wrap(sk + 1), e_k);
+          if (t < my_tiles) pv_tile<D, T>(v_addr(svs), pf, oacc);
+          if constexpr (!kShortV) refill_v(sk, svs, e_v);
         }
-      if (hh == 0) Lse[(size_t)bh * N + qrow] = lse;
+
+        // K_{t+3} and V_{t+1} must have landed for every wave before anyone
+        // reads them.  Equal rings: both were issued in iteration t+2-S, and the
+        // loads of the S-2 later iterations may stay in flight.  2-deep V ring:
+        // V_{t+1} was this iteration's first load; only its K load may stay.
+        // At a persistent boundary this iteration issued only its V load.
+        if constexpr (kShortV) wait_vmcnt<kVmPerTile>();
+        else if (PERSIST && boundary) wait_vmcnt<(2 * (kStages - 3) + 1) * kVmPerTile>();
+        else wait_vmcnt<2 * (kStages - 2) * kVmPerTile>();
+        block_sync();
+      };
+
+      // Two tiles per trip so that the two score buffers swap roles instead of
+      // being copied (and, with a 2-deep V ring, V slots are constants).
+      int t = 0, sk = ring;
+      for (; t + 1 < n_tiles; t += 2) {
+        iteration(t, sk, kShortV ? 0 : sk, sB, sA);
+        iteration(t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
+        sk = wrap(sk + 2);
+      }
+      if (t < n_tiles) iteration(t, sk, kShortV ? 0 : sk, sB, sA);
+      // The ring's last refills (clamped repeats of the last tile) are still in
+      // flight; let them land before the workgroup can end and its LDS be reused.
+      // Persistent with a next query tile: they are that tile's first loads.
+      if (!has_next) wait_vmcnt<0>();
     }
+    // Persistent: the next query tile's Q, issued before this tile's stores so
+    // that waiting for it does not wait for them.
+    if (PERSIST && has_next) load_q(nbh, nqt);
+
+    // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
+    const float l_tot = sum_halves(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // l_tot = sum_j exp2(s_j c - base_run) with base_run = m_ref c - r, where r
+    // (exact, from one FMA) is the rounding residual of base_run; hence
+    // ln sum_j exp(scale s_j) = m_ref scale + ln l_tot - r ln 2.
+    const float resid = __builtin_fmaf(m_ref, scale_log2, -base_run);
+    const float lse =
+        l_tot > 0.f ? __builtin_fmaf(m_ref, scale, logf(l_tot) - resid * kLn2) : kNegInf;
+    if (qrow < N) {
+      if (SPLIT) {
+        const size_t prow = ((size_t)split * BH + bh) * N + qrow;
+        float* orow = split_args.opart + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 o4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o4[r] = oacc[db][4 * g + r] * inv;
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) = o4;
+          }
+        if (hh == 0) split_args.lpart[prow] = lse;
+      } else {
+        uint16_t* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            T o4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o4[r] = (T)(oacc[db][4 * g + r] * inv);
+            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
+                __builtin_bit_cast(u32x2, o4);
+          }
+        if (hh == 0) Lse[(size_t)bh * N + qrow] = lse;
+      }
+    }
+    if (!PERSIST || !has_next) break;
+    ring = (ring + n_tiles) % kStages;
+    bh = nbh;
+    qt = nqt;
   }
 }
 

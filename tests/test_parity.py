@@ -101,6 +101,36 @@ def test_small_shapes(gpu_lib, case):
     compare_full(O, L, q, k, v, scale, causal, dt)
 
 
+# More causal query tiles (256 rows each) than the MI355X has CUs: these take
+# the persistent launch, where each workgroup walks several query tiles and
+# the K/V ring carries over from one to the next.  Heads a multiple of 8
+# (lists per XCD) and not; ragged N; N = 129, three key tiles per query tile,
+# the fewest the carried ring allows; N = 128 (two tiles) and the non-causal
+# cases take the plain launch.
+PERSISTENT = [
+    # (B, H, N, d, dtype, causal)
+    (4, 32, 640, 128, "bf16", True),
+    (4, 32, 640, 128, "bf16", False),
+    (3, 30, 700, 64, "bf16", True),
+    (3, 30, 700, 64, "fp16", True),
+    (1, 300, 129, 128, "bf16", True),
+    (1, 300, 129, 128, "bf16", False),
+    (2, 150, 300, 32, "fp16", True),
+    (1, 600, 128, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "b{}h{}n{}d{}-{}-{}".format(
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full"))
+def test_persistent_shapes(gpu_lib, case):
+    B, H, N, d, dt, causal = case
+    _say(f"[parity] persistent {case}")
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + H)
+    scale = 1.0 / math.sqrt(d)
+    O, L = run_gpu(gpu_lib, q, k, v, scale, causal)
+    compare_full(O, L, q, k, v, scale, causal, dt)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_logits_small_bf16(gpu_lib, causal):
     """The stress recipe (offsets of up to 20 on scaled queries) at a small size."""
