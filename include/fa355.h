@@ -170,6 +170,47 @@ int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, flo
                        float scale, int causal, void* stream, int dtype,
                        const uint8_t* block_mask, int64_t mask_heads);
 
+/*
+ * fa_bwd -- gradients of a scalar loss through O = softmax(scale Q K^T
+ * [+ causal mask]) V: given dO = dLoss/dO, returns dQ, dK and dV.  The score
+ * matrix is recomputed from Q, K and the forward's logsumexp L rather than
+ * stored (the recomputation of the Triton article "理解 Flash Attention：在
+ * Triton 中从头编写算法", section "核心思想").  With P = exp(scale S - L):
+ *     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *   Q, K, V   the forward's inputs, [B, H, N, d], element type `dtype`.
+ *   O, L      the forward's outputs for the same inputs, scale and causal
+ *             (fa_fwd's O and L).  Read only.
+ *   dO        device pointer, [B, H, N, d], element type `dtype`.  Read only.
+ *   dQ, dK, dV  device pointers, [B, H, N, d], element type `dtype`.  Written.
+ *   B, H, N, d, scale, causal, stream, dtype   as for fa_fwd; d is 32, 64 or
+ *             128 (FA_ERR_UNSUPPORTED_D otherwise).
+ *   workspace        device pointer, 256-byte aligned, owned by the caller,
+ *                    at least fa_bwd_workspace(...) bytes (float32 D, one per
+ *                    row), overwritten; nothing needs clearing before.
+ *   workspace_bytes  size of the workspace buffer.
+ * fa_bwd_workspace returns that size in bytes (4 * B * H * N), or a negative
+ * fa_status (FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D) for arguments fa_bwd rejects.
+ *
+ * Every buffer lives in device memory of the current device and stays owned
+ * by the caller.  Three kernels are enqueued on `stream` (D, then dK and dV,
+ * then dQ); the call does not synchronise.  No result is accumulated across
+ * workgroups, so identical inputs give bitwise-identical gradients.
+ *
+ * Errors: fa_fwd's checks (with O and L in the place of fa_fwd's outputs),
+ * FA_ERR_NULL for a NULL dO, dQ, dK or dV, FA_ERR_ALIGN if one of them is not
+ * 16-byte aligned, FA_ERR_WORKSPACE, and FA_ERR_ALIAS if any written buffer
+ * (dQ, dK, dV, workspace) overlaps another buffer.
+ */
+int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* L, void* dQ, void* dK, void* dV,
+           int64_t B, int64_t H, int64_t N, int64_t d,
+           float scale, int causal, void* stream, int dtype,
+           void* workspace, int64_t workspace_bytes);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

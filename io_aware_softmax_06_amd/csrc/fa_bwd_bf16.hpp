@@ -10,10 +10,11 @@
 //
 // Two kernels, so that no result is accumulated across workgroups (no
 // atomics; the output is deterministic):
-//  * fa_bwd_dkdv_bf16_kernel: a workgroup owns 128 keys (4 waves x 32) and
-//    streams the query tiles of its head; K and V sit in registers as the B
-//    operands of S = Q K^T and dP = dO V^T (one key per lane), and dV^T and
-//    dK^T accumulate from P and dS taken straight from those accumulators.
+//  * fa_bwd_dkdv_bf16_kernel: a workgroup owns 128 keys and streams the
+//    query tiles of its head; K and V sit in registers as the B operands of
+//    S = Q K^T and dP = dO V^T (one key per lane), and dV^T and dK^T
+//    accumulate from P and dS taken straight from those accumulators, in two
+//    waves per 32 keys (one per product).
 //  * fa_bwd_dq_bf16_kernel: a workgroup owns 256 queries (8 waves x 32) and
 //    streams the key tiles, like the forward: S^T = K Q^T and dP^T = V dO^T
 //    with one query per lane, then dQ^T += K^T dS^T.
@@ -22,6 +23,8 @@
 // tile read transposed (K^T, Q^T, dO^T) V-style.  Tiles are double buffered
 // with one barrier per tile.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_fwd_bf16.hpp"
 
@@ -127,9 +130,17 @@ __device__ __forceinline__ void load_row_floats(char* smem, int off, __amdgpu_bu
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch*head, 128 keys); 4 waves, 32 keys each.
-constexpr int kBwdKvWaves = 4;
-constexpr int kBwdKvKeys = 32 * kBwdKvWaves;
+// dK, dV: one workgroup per (batch*head, 128 keys), 8 waves in two roles.
+// Waves w and w + 4 share a SIMD and own the same 32 keys (key block w % 4).
+// Per query tile the dV wave forms S = Q K^T and P, and the dK wave forms
+// dP = dO V^T; the dV wave hands P (as float16) to the dK wave through LDS,
+// and after a barrier the dV wave accumulates dV^T += dO^T P while the dK
+// wave forms dS = P (dP - D) and accumulates dK^T += Q^T dS.  Each wave holds
+// half the operands and accumulators of one wave doing both products, so
+// that two waves fit on a SIMD and one wave's exponentials and conversions
+// run under the other's MFMAs.
+constexpr int kBwdKvWaves = 8;
+constexpr int kBwdKvKeys = 32 * (kBwdKvWaves / 2);
 
 template <int D>
 struct BwdKvLayout {
@@ -137,12 +148,15 @@ struct BwdKvLayout {
   static constexpr int kOffQk = 0, kOffDok = kTile, kOffQv = 2 * kTile, kOffDov = 3 * kTile;
   static constexpr int kOffL = 4 * kTile, kOffD = 4 * kTile + 256;
   static constexpr int kStage = 4 * kTile + 512;
-  static constexpr int kBytes = 2 * kStage;
+  // P of the current tile, one 4 KB slot per key block: lane l's 16-key step
+  // s2 (eight float16) at byte (s2 * 64 + l) * 16 of its block's slot.
+  static constexpr int kOffP = 2 * kStage, kPSlot = 64 * 64;
+  static constexpr int kBytes = 2 * kStage + (kBwdKvWaves / 2) * kPSlot;
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
 };
 
 template <int D, bool CAUSAL, typename T = __bf16>
-__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ Lse, const float* __restrict__ Dv,
@@ -152,16 +166,21 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   using Lay = BwdKvLayout<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int W = kBwdKvWaves;
-  constexpr int kPer = Bf16Layout<D>::kLoadsPerTile / W;  // loads per wave per tile
-  static_assert(kPer >= 1, "every wave loads a piece of every tile");
+  constexpr int kPer = Bf16Layout<D>::kLoadsPerTile >= W ? Bf16Layout<D>::kLoadsPerTile / W : 1;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int qi = lane & 31, hh = lane >> 5;
+  // The role is the same in every lane: take it from a scalar register so
+  // that the branch below is a scalar branch.
+  const bool dk_role = __builtin_amdgcn_readfirstlane(wave) >= W / 2;
+  const int kblk = wave & (W / 2 - 1);
 
   // Workgroup -> (head, key block).  Heads stay whole on one XCD; with the
-  // causal mask the first key blocks see the most queries, so they go first.
+  // causal mask the first key blocks see the most queries, so they go first
+  // (key block outermost: measured 4% faster than finishing a head's blocks
+  // before the next head's, despite the wider working set in L2).
   const int nk = (N + kBwdKvKeys - 1) / kBwdKvKeys;
   int bh, kt;
   {
@@ -185,21 +204,9 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     }
   }
   const int k0 = kt * kBwdKvKeys;
-  const int kw0 = k0 + 32 * wave;  // first key of this wave
+  const int kw0 = k0 + 32 * kblk;  // first key of this wave
   const int key = kw0 + qi;        // this lane's key
   const size_t head = (size_t)bh * N * D;
-
-  // K^T and V^T as B operands (one key per lane), fixed for the workgroup.
-  V8 kf[D / 16], vf[D / 16];
-  load_b_operand<D>(K + head, min(key, N - 1), hh, kf);
-  load_b_operand<D>(V + head, min(key, N - 1), hh, vf);
-
-  f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dkacc[i] = f32x16{};
-    dvacc[i] = f32x16{};
-  }
 
   // Query tiles: with the causal mask only those that reach this workgroup's
   // first key.
@@ -223,7 +230,11 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       const_cast<float*>(Lse + (size_t)bh * N), (short)0, N * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(Dv + (size_t)bh * N), (short)0, N * 4, kBufferWord3);
+  // This lane's 16-byte pieces of its key block's P slot.
+  u32x4* p_slot = reinterpret_cast<u32x4*>(smem + Lay::kOffP + kblk * Lay::kPSlot) + lane;
 
+  // Every wave issues its share of every tile: Q and dO both K-style (rows as
+  // A operands) and V-style (read transposed), plus L and D.
   auto load_tile = [&](int t) {
     const int st = (t & 1) * Lay::kStage, q0 = t * kBN;
     load_tile_direct<D, W>(smem, st + Lay::kOffQk, q_rsrc, q0, wave, k_off);
@@ -236,61 +247,114 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     }
   };
 
-  if (t0 < nq) load_tile(t0);
-  for (int t = t0; t < nq; ++t) {
-    wait_vmcnt<0>();
-    block_sync();  // tile t has landed for every wave; tile t-1's stage is free
-    if (t + 1 < nq) load_tile(t + 1);
-    const int q0 = t * kBN;
-    // A wave whose keys all lie after the tile's last query has nothing to do.
-    if (kw0 >= N || (CAUSAL && q0 + kBN - 1 < kw0)) continue;
-    const uint32_t st = smem_lds + (t & 1) * Lay::kStage;
+  // One role's loop: K^T (dV role) or V^T (dK role) as the B operand of its
+  // score-shaped product, one key per lane, fixed for the workgroup; the
+  // role's accumulator; two barriers per tile.  Every wave passes every
+  // barrier, also on tiles its keys do not see.
+  auto run = [&](auto dk_ic) {
+    constexpr bool DK = decltype(dk_ic)::value;
+    V8 bop[D / 16];
+    load_b_operand<D>((DK ? V : K) + head, min(key, N - 1), hh, bop);
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 
-    // S[q][key] and dP[q][key]: element 4g+r of block kb is query
-    // q0 + 32kb + key_of_row(8g + 4hh + r).
-    f32x16 sacc[2], dpacc[2];
-    score_tile<D, T>(st + Lay::kOffQk + k_lane, kf, sacc);
-    score_tile<D, T>(st + Lay::kOffDok + k_lane, vf, dpacc);
+    if (t0 < nq) load_tile(t0);
+    for (int t = t0; t < nq; ++t) {
+      wait_vmcnt<0>();
+      // Tile t has landed for every wave; tile t-1's stage is free, and so is
+      // the P slot (the dK wave read P_{t-1} before this barrier).
+      block_sync();
+      if (t + 1 < nq) load_tile(t + 1);
+      const int q0 = t * kBN;
+      // A wave whose keys all lie after the tile's last query has nothing to do.
+      const bool active = kw0 < N && !(CAUSAL && q0 + kBN - 1 < kw0);
+      const uint32_t st = smem_lds + (t & 1) * Lay::kStage;
+      const char* stage = smem + (t & 1) * Lay::kStage;
 
-    // P = exp(scale S - L), dS = P (dP - D); the four queries of a group g
-    // are consecutive, so their L and D come as one 16-byte read each.
-    const float* Lt = reinterpret_cast<const float*>(smem + (t & 1) * Lay::kStage + Lay::kOffL);
-    const float* Dt = reinterpret_cast<const float*>(smem + (t & 1) * Lay::kStage + Lay::kOffD);
-    const bool need_mask = (q0 + kBN > N) || (CAUSAL && kw0 + 31 > q0);
+      // S[q][key] (dV role) or dP[q][key] (dK role): element 4g+r of block kb
+      // is query q0 + 32kb + key_of_row(8g + 4hh + r).
+      f32x16 sacc[2];
+      V8 bf[kBN / 16];
+      if (active) {
+        score_tile<D, T>(st + (DK ? Lay::kOffDok : Lay::kOffQk) + k_lane, bop, sacc);
+        if constexpr (!DK) {
+          // P = exp(scale S - L); the four queries of a group g are
+          // consecutive, so their L values come as one 16-byte read.
+          const float* Lt = reinterpret_cast<const float*>(stage + Lay::kOffL);
+          const bool need_mask = (q0 + kBN > N) || (CAUSAL && kw0 + 31 > q0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qoff);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qoff);
+            for (int g = 0; g < 4; ++g) {
+              const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qoff);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          // -inf for a row that saw no key makes its probabilities 0.
-          const float nl = l4[r] == kNegInf ? kNegInf : -l4[r] * kLog2e;
-          float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
-          if (need_mask) {
-            const int q = q0 + qoff + r;
-            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+              for (int r = 0; r < 4; ++r) {
+                const int e = 4 * g + r;
+                // -inf for a row that saw no key makes its probabilities 0.
+                const float nl = l4[r] == kNegInf ? kNegInf : -l4[r] * kLog2e;
+                float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
+                if (need_mask) {
+                  const int q = q0 + qoff + r;
+                  if (q >= N || (CAUSAL && key > q)) p = 0.f;
+                }
+                sacc[kb][e] = p;
+              }
+            }
+          to_b_operand<T>(sacc, bf);
+          // P goes to the dK wave as float16 whatever the input type: P <= 1,
+          // and float16 keeps 11 bits of it (bfloat16 8), so dS loses nothing
+          // measurable against a float32 P.
+          f16x8 ph[kBN / 16];
+          if constexpr (std::is_same<T, _Float16>::value) {
+#pragma unroll
+            for (int s2 = 0; s2 < kBN / 16; ++s2) ph[s2] = __builtin_bit_cast(f16x8, bf[s2]);
+          } else {
+            to_b_operand<_Float16>(sacc, ph);
           }
-          sacc[kb][e] = p;
-          dpacc[kb][e] = p * (dpacc[kb][e] - d4[r]);
+#pragma unroll
+          for (int s2 = 0; s2 < kBN / 16; ++s2)
+            p_slot[64 * s2] = __builtin_bit_cast(u32x4, ph[s2]);
+          // P is in LDS before this wave reaches the barrier (the clobber
+          // keeps the stores above the wait).
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
       }
-    V8 pf[kBN / 16], dsf[kBN / 16];
-    to_b_operand<T>(sacc, pf);
-    to_b_operand<T>(dpacc, dsf);
+      block_sync();  // P of tile t is in LDS
+      if (!active) continue;
+      if constexpr (DK) {
+        // dS = P (dP - D), with P from the dV wave (float16).
+        const float* Dt = reinterpret_cast<const float*>(stage + Lay::kOffD);
+        f16x8 pp[kBN / 16];
+#pragma unroll
+        for (int s2 = 0; s2 < kBN / 16; ++s2) pp[s2] = __builtin_bit_cast(f16x8, p_slot[64 * s2]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qoff);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * g + r;
+              const float p = (float)pp[2 * kb + (e >> 3)][e & 7];
+              sacc[kb][e] = p * (sacc[kb][e] - d4[r]);
+            }
+          }
+        to_b_operand<T>(sacc, bf);
+      }
+      // dV^T += dO^T P or dK^T += Q^T dS (lane = key).
+      pv_tile<D, T>(st + (DK ? Lay::kOffQv : Lay::kOffDov) + v_lane, bf, acc);
+    }
 
-    // dV^T += dO^T P and dK^T += Q^T dS (lane = key).
-    pv_tile<D, T>(st + Lay::kOffDov + v_lane, pf, dvacc);
-    pv_tile<D, T>(st + Lay::kOffQv + v_lane, dsf, dkacc);
-  }
-
-  if (key < N) {
-    store_rows<D, T>(dK + head + (size_t)key * D, dkacc, scale, hh);
-    store_rows<D, T>(dV + head + (size_t)key * D, dvacc, 1.f, hh);
-  }
+    if (key < N) {
+      if constexpr (DK) store_rows<D, T>(dK + head + (size_t)key * D, acc, scale, hh);
+      else store_rows<D, T>(dV + head + (size_t)key * D, acc, 1.f, hh);
+    }
+  };
+  if (dk_role) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------

@@ -267,12 +267,12 @@ struct ScoreOps {
 
 // PRE: the first kAhead reads were issued by the caller (ScoreOps::issue<0..
 // kAhead-1>, in order, with no LDS operation of its own after them).
-template <int D, typename T = __bf16, bool PRE = false, typename Work = NoWork>
+template <int D, typename T = __bf16, bool PRE = false, int kAheadMax = 6, typename Work = NoWork>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
-                                           f32x16 (&sacc)[2], ScoreOps<D>& ops,
+                                           f32x16 (&sacc)[2], ScoreOps<D, kAheadMax>& ops,
                                            Work&& work = Work{}) {
   using V8 = typename Elem<T>::v8;
-  using Ops = ScoreOps<D>;
+  using Ops = ScoreOps<D, kAheadMax>;
   constexpr int kMfmas = Ops::kMfmas, kAhead = Ops::kAhead, kSlots = Ops::kSlots;
   if constexpr (!PRE)
     static_for<kAhead>([&](auto ic) { ops.template issue<decltype(ic)::value>(kaddr); });
@@ -293,10 +293,10 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T
   });
 }
 
-template <int D, typename T = __bf16, typename Work = NoWork>
+template <int D, typename T = __bf16, int kAheadMax = 6, typename Work = NoWork>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
                                            f32x16 (&sacc)[2], Work&& work = Work{}) {
-  ScoreOps<D> ops;
+  ScoreOps<D, kAheadMax> ops;
   score_tile<D, T, false>(kaddr, qf, sacc, ops, work);
 }
 

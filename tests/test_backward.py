@@ -10,7 +10,10 @@ Tolerance (no figure is set for gradients, so it follows the arithmetic):
 each of dQ, dK, dV must satisfy max |g - g_ref| <= tol * max |g_ref| with
 tol = 2e-2 for bfloat16 (P and dS enter the products rounded to bf16, 2^-9
 relative, and the outputs are rounded to bf16), 1e-2 for float16 (2^-11) and
-tol = 1e-4 for float32.
+tol = 1e-4 for float32.  The largest bf16 term is D = rowsum(dO o O) taken
+from the forward's bf16 O: where P is peaked, dP - D cancels and carries
+O's rounding into dS.  On the large-logit case it alone puts dK near 1.4e-2
+(a float64 emulation of the same roundings), which the kernels match.
 """
 
 import math
