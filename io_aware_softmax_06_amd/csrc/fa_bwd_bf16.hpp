@@ -234,23 +234,35 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   u32x4* p_slot = reinterpret_cast<u32x4*>(smem + Lay::kOffP + kblk * Lay::kPSlot) + lane;
 
   // Every wave issues its share of every tile: Q and dO both K-style (rows as
-  // A operands) and V-style (read transposed), plus L and D.
-  auto load_tile = [&](int t) {
+  // A operands) and V-style (read transposed), plus L and D.  The V-style Q
+  // goes separately (load_qv): the dK wave reads it one iteration late.
+  auto load_main = [&](int t) {
     const int st = (t & 1) * Lay::kStage, q0 = t * kBN;
     load_tile_direct<D, W>(smem, st + Lay::kOffQk, q_rsrc, q0, wave, k_off);
     load_tile_direct<D, W>(smem, st + Lay::kOffDok, do_rsrc, q0, wave, k_off);
-    load_tile_direct<D, W>(smem, st + Lay::kOffQv, q_rsrc, q0, wave, v_off);
     load_tile_direct<D, W>(smem, st + Lay::kOffDov, do_rsrc, q0, wave, v_off);
     if (wave == 0) {
       load_row_floats(smem, st + Lay::kOffL, l_rsrc, q0, lane);
       load_row_floats(smem, st + Lay::kOffD, d_rsrc, q0, lane);
     }
   };
+  auto load_qv = [&](int t) {
+    load_tile_direct<D, W>(smem, (t & 1) * Lay::kStage + Lay::kOffQv, q_rsrc, t * kBN, wave,
+                           v_off);
+  };
 
   // One role's loop: K^T (dV role) or V^T (dK role) as the B operand of its
   // score-shaped product, one key per lane, fixed for the workgroup; the
   // role's accumulator; two barriers per tile.  Every wave passes every
   // barrier, also on tiles its keys do not see.
+  //
+  // Software pipeline of the dK wave: it forms dS of tile t after the second
+  // barrier and accumulates Q_t^T dS_t only in the first half of iteration
+  // t+1, under the dV wave's exponentials.  So the V-style Q_t must stay
+  // until the second barrier of iteration t+1: it is loaded after the second
+  // barrier of iteration t-1 (into the stage of tile t-1, whose V-style Q the
+  // dK wave has just used), and the wait at the top of an iteration lets that
+  // one load stay in flight.
   auto run = [&](auto dk_ic) {
     constexpr bool DK = decltype(dk_ic)::value;
     V8 bop[D / 16];
@@ -258,14 +270,21 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     f32x16 acc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+    V8 bf[kBN / 16];    // P (dV role) or dS (dK role) as B operands
+    bool held = false;  // dK role: bf holds dS of the previous tile
 
-    if (t0 < nq) load_tile(t0);
+    if (t0 < nq) {
+      load_main(t0);
+      load_qv(t0);
+    }
     for (int t = t0; t < nq; ++t) {
-      wait_vmcnt<0>();
-      // Tile t has landed for every wave; tile t-1's stage is free, and so is
-      // the P slot (the dK wave read P_{t-1} before this barrier).
+      // Tile t has landed for every wave, and so has the V-style Q of tile
+      // t-1; only tile t's own V-style Q may be in flight.  Tile t-1's stage
+      // is free except for its V-style Q, and so is the P slot (the dK wave
+      // read P_{t-1} before this barrier).
+      wait_vmcnt<kPer>();
       block_sync();
-      if (t + 1 < nq) load_tile(t + 1);
+      if (t + 1 < nq) load_main(t + 1);
       const int q0 = t * kBN;
       // A wave whose keys all lie after the tile's last query has nothing to do.
       const bool active = kw0 < N && !(CAUSAL && q0 + kBN - 1 < kw0);
@@ -275,7 +294,6 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       // S[q][key] (dV role) or dP[q][key] (dK role): element 4g+r of block kb
       // is query q0 + 32kb + key_of_row(8g + 4hh + r).
       f32x16 sacc[2];
-      V8 bf[kBN / 16];
       if (active) {
         score_tile<D, T>(st + (DK ? Lay::kOffDok : Lay::kOffQk) + k_lane, bop, sacc);
         if constexpr (!DK) {
@@ -321,7 +339,14 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
       }
-      block_sync();  // P of tile t is in LDS
+      if constexpr (DK) {
+        // dK^T += Q_{t-1}^T dS_{t-1} (lane = key), from the previous stage.
+        if (held)
+          pv_tile<D, T>(smem_lds + ((t - 1) & 1) * Lay::kStage + Lay::kOffQv + v_lane, bf, acc);
+        held = false;
+      }
+      block_sync();  // P of tile t is in LDS; the V-style Q of tile t-1 is read
+      if (t + 1 < nq) load_qv(t + 1);
       if (!active) continue;
       if constexpr (DK) {
         // dS = P (dP - D), with P from the dV wave (float16).
@@ -343,9 +368,19 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             }
           }
         to_b_operand<T>(sacc, bf);
+        held = true;
+      } else {
+        // dV^T += dO^T P (lane = key).
+        pv_tile<D, T>(st + Lay::kOffDov + v_lane, bf, acc);
       }
-      // dV^T += dO^T P or dK^T += Q^T dS (lane = key).
-      pv_tile<D, T>(st + (DK ? Lay::kOffQv : Lay::kOffDov) + v_lane, bf, acc);
+    }
+    // The last tile's V-style Q: every wave's share has landed before the
+    // dK wave reads it.
+    wait_vmcnt<0>();
+    block_sync();
+    if constexpr (DK) {
+      if (held)
+        pv_tile<D, T>(smem_lds + ((nq - 1) & 1) * Lay::kStage + Lay::kOffQv + v_lane, bf, acc);
     }
 
     if (key < N) {
