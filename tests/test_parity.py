@@ -131,6 +131,25 @@ def test_persistent_shapes(gpu_lib, case):
     compare_full(O, L, q, k, v, scale, causal, dt)
 
 
+@pytest.mark.parametrize("case", [(4, 32, 640, 128, "bf16"), (3, 30, 700, 64, "fp16"),
+                                  (1, 300, 129, 128, "bf16")],
+                         ids=lambda c: "b{}h{}n{}d{}-{}".format(*c))
+def test_persistent_bitwise_equals_one_workgroup_per_tile(gpu_lib, case):
+    """The persistent causal launch carries the K/V ring from one query tile
+    to the next; every tile must still see exactly its own keys.  A one-range
+    split runs the same per-tile arithmetic with one workgroup per query tile
+    and is bitwise equal to it (a single wrong or stale K/V tile would not be)."""
+    B, H, N, d, dt = case
+    _say(f"[parity] persistent bitwise {case}")
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + 1, device="cuda")
+    O1, L1 = gpu_lib.fwd(q, k, v, causal=True)
+    O2, L2, _ = gpu_lib.fwd_splitkv(q, k, v, 1, causal=True)
+    O3, L3 = gpu_lib.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    assert torch.equal(O1, O3) and torch.equal(L1, L3)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_logits_small_bf16(gpu_lib, causal):
     """The stress recipe (offsets of up to 20 on scaled queries) at a small size."""
