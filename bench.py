@@ -70,7 +70,8 @@ def visible_pairs(mask, N, causal, block=64):
 
 # The sources the forward kernels and their launches are built from; a
 # change to any of them makes a recorded traffic figure stale.
-FORWARD_SOURCES = ("fa355.hip", "fa_common.hpp", "fa_fwd_bf16.hpp", "fa_fwd_f32.hpp", "fa_merge.hpp")
+FORWARD_SOURCES = ("fa355.hip", "fa355_w4.hip", "fa_common.hpp", "fa_fwd_bf16.hpp",
+                   "fa_fwd_f32.hpp", "fa_merge.hpp")
 
 
 def kernel_source_digest():

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa355.so")
-SOURCES = [os.path.join(CSRC, "fa355.hip"), os.path.join(CSRC, "fa355_d256.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa355.hip", "fa355_d256.hip", "fa355_w4.hip")]
 DEPENDS = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, "fa355.h")]
 
 HIPCC_FLAGS = [

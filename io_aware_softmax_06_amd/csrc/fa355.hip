@@ -17,6 +17,7 @@
 #include "fa_bwd_bf16.hpp"
 #include "fa_bwd_f32.hpp"
 #include "fa355_d256.h"
+#include "fa355_w4.h"
 
 namespace {
 
@@ -110,6 +111,9 @@ hipError_t prepare_bf16() {
 #ifndef FA355_PERSIST
 #define FA355_PERSIST 1
 #endif
+#ifndef FA355_W4
+#define FA355_W4 1
+#endif
 
 // Compute units of the current device (0 if the query fails), cached per device.
 int device_cus() {
@@ -201,6 +205,18 @@ hipError_t launch_forward(const void* Q, const void* K, const void* V, void* O, 
   if (d == 256)
     return causal ? launch_f32<256, true, MODE>(Q, K, V, O, L, BH, N, scale, sa, s)
                   : launch_f32<256, false, MODE>(Q, K, V, O, L, BH, N, scale, sa, s);
+  // Dense 16-bit launches whose 256-row tiles would leave CUs idle take the
+  // 128-row build (fa355_w4.hip): fewer tiles than CUs, or, under the causal
+  // mask, where the longest tile sets the time, no more tiles than CUs.
+  if constexpr (MODE == fa355::kDense && FA355_W4) {
+    if (dtype != FA_F32) {
+      const int cus = device_cus();
+      const int64_t tiles = BH * ((N + fa355::kBM - 1) / fa355::kBM);
+      if (cus > 0 && (tiles < cus || (causal && tiles <= cus)))
+        return fa355_w4_forward(Q, K, V, O, L, BH, N, d, scale, causal, dtype == FA_F16 ? 1 : 0,
+                                s);
+    }
+  }
   if (dtype == FA_BF16) return launch_mfma<MODE, __bf16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (dtype == FA_F16) return launch_mfma<MODE, _Float16>(Q, K, V, O, L, BH, N, d, scale, causal, sa, s);
   if (d == 32)

@@ -150,6 +150,23 @@ def test_persistent_bitwise_equals_one_workgroup_per_tile(gpu_lib, case):
     assert torch.equal(O1, O3) and torch.equal(L1, L3)
 
 
+@pytest.mark.parametrize("case", [(1, 3, 1000, 128, "bf16", True), (2, 2, 513, 64, "fp16", False),
+                                  (1, 2, 300, 32, "bf16", True), (1, 4, 8192, 128, "bf16", False)],
+                         ids=lambda c: "b{}h{}n{}d{}-{}-{}".format(
+                             c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full"))
+def test_few_tiles_bitwise_equals_256_row_workgroups(gpu_lib, case):
+    """Launches with fewer 256-row tiles than CUs run 128-row workgroups; a
+    row's arithmetic does not depend on the workgroup's height, so the result
+    is bitwise that of the 256-row kernel (here as a one-range split)."""
+    B, H, N, d, dt, causal = case
+    _say(f"[parity] few tiles bitwise {case}")
+    q, k, v = make_qkv(B, H, N, d, TORCH_DTYPE[dt], seed=N + 2, device="cuda")
+    O1, L1 = gpu_lib.fwd(q, k, v, causal=causal)
+    O2, L2, _ = gpu_lib.fwd_splitkv(q, k, v, 1, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_logits_small_bf16(gpu_lib, causal):
     """The stress recipe (offsets of up to 20 on scaled queries) at a small size."""
