@@ -186,9 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--splits", type=int, default=0,
-                    help="key ranges of the split path (default: the workload's own; "
-                         "0 for a workload without one runs fa_fwd)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="key ranges of the split path (default: the workload's own, if it "
+                         "has one; 0 runs fa_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB "
@@ -226,7 +226,7 @@ def main():
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
         bwd_ws = torch.empty(fa.fa_bwd_workspace(w.B, w.H, w.N, w.d), dtype=torch.uint8,
                              device=dev)
-    splits = args.splits or workloads.SPLITS_OF.get(w.name, 0)
+    splits = workloads.SPLITS_OF.get(w.name, 0) if args.splits is None else args.splits
     ws = None
     if splits:
         need = fa.fa_fwd_splitkv_workspace(w.B, w.H, w.N, w.d, splits)

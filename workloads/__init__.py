@@ -58,14 +58,22 @@ STRESS = Workload("stress_bf16_b16h16n2048d64", 16, 16, 2048, 64, "bf16", False,
 
 ALL = (TINY_FP32, MULTIHEAD, CAUSAL_4K, LONG_16K, STRESS)
 
-# Key-range split workloads: few query tiles per head, so one workgroup per
-# 256-row query tile covers only part of the chip's 256 compute units.  Each
-# entry names the shape and the number of key ranges the split path uses.
+# Few query tiles: 32 or 64 tiles of 256 rows cover only part of the chip's
+# 256 compute units, so fa_fwd runs them as 128-row workgroups, two per CU.
 LOWOCC_8K = Workload("lowocc_bf16_b1h4n8192d128", 1, 4, 8192, 128, "bf16", False)
 LOWOCC_8K_CAUSAL = Workload("lowocc_causal_bf16_b1h8n8192d128", 1, 8, 8192, 128, "bf16", True)
-SPLIT = ((LOWOCC_8K, 4), (LOWOCC_8K_CAUSAL, 4))
+FEW_TILES = (LOWOCC_8K, LOWOCC_8K_CAUSAL)
 
-BY_NAME = {w.name: w for w in ALL + tuple(w for w, _ in SPLIT)}
+# Key-range split workloads: a single head at N = 16384, where even 128-row
+# workgroups leave half the CUs idle (and, causal, the last query tile alone
+# streams every key).  Each entry names the shape and the number of key
+# ranges the split path uses.
+ONEHEAD_16K = Workload("lowocc_bf16_b1h1n16384d128", 1, 1, 16384, 128, "bf16", False)
+ONEHEAD_16K_CAUSAL = Workload("lowocc_causal_bf16_b1h1n16384d128", 1, 1, 16384, 128, "bf16",
+                              True)
+SPLIT = ((ONEHEAD_16K, 4), (ONEHEAD_16K_CAUSAL, 8))
+
+BY_NAME = {w.name: w for w in ALL + FEW_TILES + tuple(w for w, _ in SPLIT)}
 SPLITS_OF = {w.name: s for w, s in SPLIT}
 
 # The stress workload: Q and K drawn with standard deviation 3, and a per-row
