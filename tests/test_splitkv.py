@@ -71,7 +71,7 @@ def check_partials(fa, ws, S, q, k, v, scale, causal, dtype):
             assert np.array_equal(np.isneginf(Lg), ~live), f"{where}: empty rows differ"
             assert np.isfinite(Og).all()
             eo = np.abs(Og - O_ref).max()
-            el = np.abs(np.where(live, Lg - L_ref, 0.0)).max()
+            el = np.abs(np.where(live, Lg, 0.0) - np.where(live, L_ref, 0.0)).max()
             assert eo <= TOL_O[dtype], f"{where}: max |O_s - ref| = {eo}"
             assert el <= TOL_L, f"{where}: max |L_s - ref| = {el}"
 
