@@ -1,0 +1,63 @@
+"""Host-side checks of the measurement harness (no GPU).
+
+bench.py measures one GPU only and must refuse more; the committed rocprofv3
+summaries must name the command that made them and, for the HBM counters,
+carry every field bench.py reads.
+"""
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr or "single" in res.stderr
+    assert res.stdout.strip() == ""  # no JSON line
+
+
+def _summaries():
+    return sorted(f for f in os.listdir(PROFILES) if f.endswith(".txt"))
+
+
+@pytest.mark.parametrize("name", _summaries())
+def test_summary_names_its_command(name):
+    text = open(os.path.join(PROFILES, name)).read()
+    cmd = [line for line in text.splitlines() if line.startswith("command")]
+    assert cmd, f"{name}: no command line"
+    assert "rocprofv3" in cmd[0] and "bench.py" in cmd[0]
+    assert "_work" not in text  # only committed files are run
+
+
+@pytest.mark.parametrize("name", [f for f in _summaries() if f.startswith("hbm_traffic_")])
+def test_traffic_summary_is_consistent(name):
+    fields = {}
+    for line in open(os.path.join(PROFILES, name)):
+        m = re.match(r"^(\w+):\s*(.+)$", line.strip())
+        if m:
+            fields[m.group(1)] = m.group(2)
+    for key in ("fetch_factor", "write_factor", "kernel_fetch_kib_per_dispatch",
+                "kernel_write_kib_per_dispatch", "fetch_bytes_per_launch",
+                "write_bytes_per_launch", "traffic_bytes_per_launch", "source_digest"):
+        assert key in fields, f"{name}: missing {key}"
+    fetch_f, write_f = float(fields["fetch_factor"]), float(fields["write_factor"])
+    # FETCH_SIZE counts half of a plain copy's reads on this chip, WRITE_SIZE all
+    # of its writes; the calibration copy fixes both factors.
+    assert 1.5 < fetch_f < 2.5 and 0.8 < write_f < 1.2
+    kf = [float(x) for x in fields["kernel_fetch_kib_per_dispatch"].split()]
+    kw = [float(x) for x in fields["kernel_write_kib_per_dispatch"].split()]
+    fb = sum(kf) / len(kf) * 1024 * fetch_f
+    wb = sum(kw) / len(kw) * 1024 * write_f
+    # the factors are printed to 5 decimals: agree to 1e-5 relative
+    assert fb == pytest.approx(float(fields["fetch_bytes_per_launch"]), rel=1e-5)
+    assert wb == pytest.approx(float(fields["write_bytes_per_launch"]), rel=1e-5)
+    assert float(fields["traffic_bytes_per_launch"]) == pytest.approx(
+        float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"]), abs=2)
