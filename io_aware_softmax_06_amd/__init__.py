@@ -155,6 +155,13 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
+def _on_device(dev):
+    """Context making ``dev`` the current HIP device: the library launches
+    on the calling thread's current device, which must hold the tensors."""
+    import torch
+    return torch.cuda.device(dev)
+
+
 def _prepare(q, k, v, scale, out, lse, stream):
     import torch
     if q.dim() != 4:
@@ -191,8 +198,9 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     (default: torch's current stream) and does not synchronise.
     """
     (B, H, N, d), scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q))
+    with _on_device(q.device):
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q))
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
@@ -218,10 +226,11 @@ def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, out=None, lse=Non
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                        lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
-                        stream.cuda_stream, _dtype_code(q), num_splits, workspace.data_ptr(),
-                        ws_bytes)
+    with _on_device(q.device):
+        rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                            stream.cuda_stream, _dtype_code(q), num_splits,
+                            workspace.data_ptr(), ws_bytes)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse, workspace
@@ -262,9 +271,10 @@ def fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse
         mask_heads = B * H
     else:
         raise ValueError(f"block_mask must be [{nb}, {nb}], [H, {nb}, {nb}] or [B, H, {nb}, {nb}]")
-    rc = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
-                            stream.cuda_stream, _dtype_code(q), m.data_ptr(), mask_heads)
+    with _on_device(q.device):
+        rc = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                                stream.cuda_stream, _dtype_code(q), m.data_ptr(), mask_heads)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
@@ -295,11 +305,14 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=None
         raise FaError(need)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
-                B, H, N, d, scale, 1 if causal else 0, stream.cuda_stream, _dtype_code(q),
-                workspace.data_ptr(), ws_bytes)
+    with _on_device(q.device):
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                    lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                    grads[2].data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                    stream.cuda_stream, _dtype_code(q), workspace.data_ptr(), ws_bytes)
     if rc != FA_OK:
         raise FaError(rc)
     return tuple(grads)
