@@ -865,10 +865,15 @@ fa_fwd_bf16_kernel(
       // One tile.  On entry pf holds P_t and cur the raw scores of tile t+1;
       // nxt receives tile t+2.  sk = t % kStages is the K ring position (K_{t+2}
       // is in slot (sk+2) % kStages); svs = t % kVStages is V_t's slot.
-      // The loads of later tiles are issued inside the two MFMA phases rather
-      // than all at the top: eight waves issuing them at once right after the
-      // barrier queue up in the address unit.  With a 2-deep V ring the V load
-      // goes first, so that it has the whole iteration to land.
+      // The loads of later tiles are issued between the P V MFMAs (the V load
+      // after the third, the K load half way) rather than all at the top:
+      // eight waves issuing them at once right after the barrier queue up in
+      // the address unit.  Issued there, their LDS writes tend to land during
+      // the score phase, whose b128 operand reads leave LDS bandwidth to spare,
+      // rather than during the P V phase, whose transposing reads need about
+      // all of it (V issued in the score phase measured 0.4-1% slower).  With
+      // a 2-deep V ring the V load goes first, so that it has the whole
+      // iteration to land.
       constexpr bool kShortV = kVStages == 2;
       auto refill_v = [&](int sk, int svs, uint32_t ev) {
         if constexpr (kShortV) load_v(svs ^ 1, ev);
@@ -891,7 +896,7 @@ fa_fwd_bf16_kernel(
         if (t + 1 < my_tiles) {
           mask_tile(e_next, cur);
           // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
-          // the K load of a later tile in the middle.
+          // the V and K loads of later tiles issued early and in the middle.
           SoftmaxState st;
           // The last MFMAs of this phase issue the first operand reads of the
           // score phase (K_{t+2} has been valid since the last barrier).
@@ -903,6 +908,7 @@ fa_fwd_bf16_kernel(
             run_steps(ic, std::integral_constant<int, kStage1Steps>{},
                       [&](auto sic) { stage1_step(sic, cur, st); });
             if constexpr (kShortV && c == 0) refill_v(sk, svs, e_v);
+            if constexpr (!kShortV && c == 2) refill_v(sk, svs, e_v);
             if constexpr (c == kMf / 2) load_k(wrap(sk + 1), e_k);
             if constexpr (kPre > 0 && c >= kMf - kPre)
               sops.template issue<c - (kMf - kPre)>(k_next);
@@ -916,12 +922,10 @@ fa_fwd_bf16_kernel(
             for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
           }
 
-          // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU),
-          // with the V load of a later tile in the middle.
+          // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU).
           score_tile<D, T, kXPhase>(k_next, qf, nxt, sops, [&](auto ic) {
             run_steps(ic, std::integral_constant<int, kStage2Steps>{},
                       [&](auto sic) { stage2_step(sic, cur, st, pf); });
-            if constexpr (!kShortV && decltype(ic)::value == kMf / 2) refill_v(sk, svs, e_v);
           });
           pin_probs(pf);
         } else {
