@@ -2,7 +2,7 @@
 """Throughput of the attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--splits S] [--no-cpu-baseline]
+                    [--splits S] [--no-cpu-baseline] [--graph]
 
 One step is one fa_fwd call (the whole forward: QK^T, online softmax, PV,
 normalisation, O and L written) over one batch of seeded synthetic inputs
@@ -24,6 +24,10 @@ For the key-range split workloads (few query tiles per head) a step is one
 fa_fwd_splitkv call instead: the split kernel and the merge kernel, with the
 workspace allocated before the timed region.  The line then also carries the
 unsplit fa_fwd time on the same inputs for comparison (`unsplit`).
+
+With --graph the K timed steps are captured into one HIP graph and the
+timed region is one replay of it (launch overhead between steps removed);
+the default is K eager calls.
 
 Prints ONE JSON line.  `value` is attention TFLOP/s with the conventional
 count 4*B*H*N^2*d (halved for causal) over the timed steps' wall time.
@@ -190,6 +194,9 @@ def main():
                     help="key ranges of the split path (default: the workload's own, if it "
                          "has one; 0 runs fa_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps into one HIP graph (torch.cuda.graph) "
+                         "and time one replay of it instead of K eager calls")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB "
                          "(read once, written once) so that a counter run can scale its HBM "
@@ -212,6 +219,9 @@ def main():
     O = torch.empty_like(q)
     L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # The library launches on the stream it is given; under graph capture that
+    # must be the capture stream, which the binding picks when given None.
+    call_stream = None if args.graph else stream
     sparse_mask = None
     flops = attention_flops(w)
     if w.name == workloads.SPARSE_4K.name:
@@ -235,19 +245,19 @@ def main():
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def unsplit_step():
-        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L, stream=stream)
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L, stream=call_stream)
 
     def split_step():
         fa.fwd_splitkv(q, k, v, splits, scale=w.scale, causal=w.causal, out=O, lse=L,
-                       workspace=ws, stream=stream)
+                       workspace=ws, stream=call_stream)
 
     def sparse_step():
         fa.fwd_blocksparse(q, k, v, sparse_mask, scale=w.scale, causal=w.causal, out=O, lse=L,
-                           stream=stream)
+                           stream=call_stream)
 
     def backward_step():
         fa.bwd(q, k, v, O, do, L, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
-               workspace=bwd_ws, stream=stream)
+               workspace=bwd_ws, stream=call_stream)
 
     step = (backward_step if backward else sparse_step if sparse_mask is not None
             else split_step if splits else unsplit_step)
@@ -273,11 +283,32 @@ def main():
         wall_s = time.perf_counter() - t0
         return wall_s, start.elapsed_time(end) / 1e3 / n
 
+    def timed_graph(fn, n):
+        """As timed(), for one replay of a graph that holds n calls."""
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for _ in range(n):
+                fn()
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        return wall_s, start.elapsed_time(end) / 1e3 / n
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    wall, avg_launch_s = timed(step, args.steps)
+    wall, avg_launch_s = (timed_graph if args.graph else timed)(step, args.steps)
+    call_stream = stream  # the comparison runs below are eager
 
     dense = None
     if sparse_mask is not None:  # after the timed region: every pair, on the same inputs
@@ -333,6 +364,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "layout": "[B,H,N,d]",
                    "parallelism": "single GPU",
+                   "launch": "one HIP graph of the K steps" if args.graph else "eager",
                    "entry_point": ("fa_bwd" if backward else
                                    "fa_fwd_blocksparse" if sparse_mask is not None
                                    else "fa_fwd_splitkv" if splits else "fa_fwd"),
