@@ -32,12 +32,28 @@ struct Elem<__bf16> {
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // acc + x[2i] + x[2i+1] in float32 (v_dot2c_f32_bf16 against (1, 1)).
+  template <int I>
+  static __device__ __forceinline__ float add_pair(v8 x, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 pair = {x[2 * I], x[2 * I + 1]};
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+  }
 };
 template <>
 struct Elem<_Float16> {
   using v8 = f16x8;
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // acc + x[2i] + x[2i+1] in float32 (v_dot2c_f32_f16 against (1, 1)).
+  template <int I>
+  static __device__ __forceinline__ float add_pair(v8 x, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 pair = {x[2 * I], x[2 * I + 1]};
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(pair, one, acc, false);
   }
 };
 

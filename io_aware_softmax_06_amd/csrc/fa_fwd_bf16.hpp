@@ -613,7 +613,8 @@ fa_fwd_bf16_kernel(
     // score it came from.  -FLT_MAX marks "no visible key yet".
     float base_run = -__FLT_MAX__;
     float m_ref = kNegInf;
-    float l_run = 0.f;  // this half-wave's part of the denominator
+    float l_run = 0.f;   // this half-wave's part of the denominator (float32 P)
+    float lh_run = 0.f;  // the same sum over P as rounded for the P V MFMAs
 
     const __amdgpu_buffer_rsrc_t k_rsrc = head_resource(Kb, N * D * 2);
     const __amdgpu_buffer_rsrc_t v_rsrc = head_resource(Vb, N * D * 2);
@@ -683,13 +684,24 @@ fa_fwd_bf16_kernel(
     // (two per step), the half-wave exchange and reference update, eight pairs
     // of exponentials of block 0, their sum.
     // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
-    // into l_run, eight pairs of bf16 conversions into the P^T operands.  The
-    // sums are taken over the float32 probabilities: summing their bf16
-    // roundings instead would move L by up to 2^-9 on rows with few keys.
+    // into l_run, eight pairs of bf16 conversions into the P^T operands (whose
+    // rounded values are summed into lh_run during that tile's P V MFMAs,
+    // lh_step below).  L takes the sum of the float32 probabilities (l_run):
+    // the sum of their bf16 roundings would move L by up to 2^-8 on rows with
+    // few keys.  O is divided by the sum of the rounded values (lh_run), the
+    // weights the P V MFMAs actually applied, so that O is their convex
+    // combination of V rows: divided by l_run instead, a row dominated by one
+    // key carries that key's rounding error (up to 2^-8 |v|) into O on top of
+    // O's own bf16 rounding, which exceeded 2e-2 on rows with |O| near 4 under
+    // the large-logits workload.
     struct SoftmaxState {
       float m, alpha, half_sum;
       bool need;
     };
+    // Factor that moves lh_run to the reference of the tile whose P^T is in
+    // the P V operands (that tile's alpha); set with P^T, used when its
+    // rounded values are summed during that tile's P V MFMAs.
+    float lh_alpha = 1.f;
     constexpr int kStage1Steps = 18, kStage2Steps = 17;
     auto stage1_step = [&](auto sic, f32x16(&sc)[2], SoftmaxState& st) {
       constexpr int sidx = decltype(sic)::value;
@@ -736,7 +748,18 @@ fa_fwd_bf16_kernel(
         constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
 #pragma unroll
         for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (T)sc[s2 >> 1][8 * (s2 & 1) + j];
+        if constexpr (k == 7) lh_alpha = st.alpha;
       }
+    };
+    // The sum of the rounded P^T operands pfo into lh_run, as 8 steps (two
+    // pairs each) that run under the P V MFMAs reading those operands.
+    constexpr int kLhSteps = 8;
+    auto lh_step = [&](auto sic, const V8(&pfo)[kBN / 16]) {
+      constexpr int k = decltype(sic)::value;
+      constexpr int s2 = k >> 1, p0 = 2 * (k & 1);
+      if constexpr (k == 0) lh_run *= lh_alpha;
+      lh_run = Elem<T>::template add_pair<p0>(pfo[s2], lh_run);
+      lh_run = Elem<T>::template add_pair<p0 + 1>(pfo[s2], lh_run);
     };
     // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
     auto run_steps = [&](auto ic, auto nsteps_ic, auto&& step) {
@@ -776,7 +799,7 @@ fa_fwd_bf16_kernel(
         pin(w);
         pfo[s2] = __builtin_bit_cast(V8, w);
       }
-      asm volatile("" : "+v"(l_run));
+      asm volatile("" : "+v"(l_run), "+v"(lh_run));
     };
 
     // A workgroup whose key range is empty (a split past the causal diagonal)
@@ -907,6 +930,8 @@ fa_fwd_bf16_kernel(
             constexpr int c = decltype(ic)::value;
             run_steps(ic, std::integral_constant<int, kStage1Steps>{},
                       [&](auto sic) { stage1_step(sic, cur, st); });
+            run_steps(ic, std::integral_constant<int, kLhSteps>{},
+                      [&](auto sic) { lh_step(sic, pf); });
             if constexpr (kShortV && c == 0) refill_v(sk, svs, e_v);
             if constexpr (!kShortV && c == 2) refill_v(sk, svs, e_v);
             if constexpr (c == kMf / 2) load_k(wrap(sk + 1), e_k);
@@ -935,7 +960,10 @@ fa_fwd_bf16_kernel(
           // The next prologue issues it after its first scores, as every
           // prologue does.
           if (!(PERSIST && boundary)) load_k(wrap(sk + 1), e_k);
-          if (t < my_tiles) pv_tile<D, T>(v_addr(svs), pf, oacc);
+          if (t < my_tiles) {
+            pv_tile<D, T>(v_addr(svs), pf, oacc);
+            static_for<kLhSteps>([&](auto sic) { lh_step(sic, pf); });
+          }
           if constexpr (!kShortV) refill_v(sk, svs, e_v);
         }
 
@@ -970,7 +998,7 @@ fa_fwd_bf16_kernel(
 
     // Epilogue: O^T element 4g+r of block db is O[qrow][32db + 8g + 4hh + r].
     const float l_tot = sum_halves(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? 1.f / sum_halves(lh_run) : 0.f;
     // l_tot = sum_j exp2(s_j c - base_run) with base_run = m_ref c - r, where r
     // (exact, from one FMA) is the rounding residual of base_run; hence
     // ln sum_j exp(scale s_j) = m_ref scale + ln l_tot - r ln 2.
