@@ -463,6 +463,7 @@ fa_fwd_bf16_kernel(
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
   constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)
+  constexpr bool kLhInPv = D <= 64;                 // where the rounded-P sum is taken (lh_step)
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -748,12 +749,21 @@ fa_fwd_bf16_kernel(
         constexpr int s2 = k >> 1, j0 = 4 * (k & 1);
 #pragma unroll
         for (int j = j0; j < j0 + 4; ++j) pfo[s2][j] = (T)sc[s2 >> 1][8 * (s2 & 1) + j];
-        if constexpr (k == 7) lh_alpha = st.alpha;
+        if constexpr (kLhInPv) {
+          if constexpr (k == 7) lh_alpha = st.alpha;
+        } else {
+          if constexpr (k == 0) lh_run *= st.alpha;
+          lh_run = Elem<T>::template add_pair<j0 / 2>(pfo[s2], lh_run);
+          lh_run = Elem<T>::template add_pair<j0 / 2 + 1>(pfo[s2], lh_run);
+        }
       }
     };
     // The sum of the rounded P^T operands pfo into lh_run, as 8 steps (two
-    // pairs each) that run under the P V MFMAs reading those operands.
-    constexpr int kLhSteps = 8;
+    // pairs each) that run under the P V MFMAs reading those operands; at
+    // d = 128 and 256 it is taken right after each conversion instead (kLhInPv
+    // false), which measured faster there (d = 64 is VALU-bound and gains from
+    // moving the work into the P V phase).
+    constexpr int kLhSteps = kLhInPv ? 8 : 0;
     auto lh_step = [&](auto sic, const V8(&pfo)[kBN / 16]) {
       constexpr int k = decltype(sic)::value;
       constexpr int s2 = k >> 1, p0 = 2 * (k & 1);
