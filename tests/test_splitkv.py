@@ -178,6 +178,28 @@ def test_split_workload(gpu_lib, ws):
     _sampled_check(gpu_lib, w, S, seed=1)
 
 
+def test_split_large_logits_every_row(gpu_lib):
+    """The large-logits workload through four key ranges, every row against the
+    oracle: each range's partial output is normalised by the sum of its own
+    rounded probabilities and the merge weighs the ranges by their float32 L_s,
+    which must keep the rows dominated by one key inside the bound."""
+    w, S = workloads.STRESS, 4
+    _say(f"[splitkv] every row: {w.describe()} splits={S}")
+    q, k, v = workloads.make_inputs(w, 1)
+    O, L, _ = gpu_lib.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), S, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    Og, Lg = to_f64_numpy(O), L.cpu().double().numpy()
+    qn, kn, vn = to_f64_numpy(q), to_f64_numpy(k), to_f64_numpy(v)
+    eo = el = 0.0
+    for b in range(w.B):
+        Or, Lr = oracle.attention(qn[b:b + 1], kn[b:b + 1], vn[b:b + 1], w.scale, w.causal)
+        eo = max(eo, float(np.abs(Og[b:b + 1] - Or).max()))
+        el = max(el, float(np.abs(Lg[b:b + 1] - Lr).max()))
+    _say(f"[splitkv]   all {w.B * w.H * w.N} rows: max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= TOL_O[w.dtype]
+    assert el <= TOL_L
+
+
 def test_split_long_sequence_eight_ranges(gpu_lib):
     """N = 16384 cut into 8 key ranges (one GPU's share of an 8-way key split)."""
     w = workloads.LONG_16K
