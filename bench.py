@@ -375,7 +375,7 @@ def main():
                    **({"num_splits": splits} if splits else {})},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "bound": "mfma",
+            "bound": "alu" if w.dtype == "fp32" else "mfma",
             "achieved": round(achieved, 3),
             "peak": peak,
             "unit": "TFLOP/s",
