@@ -169,7 +169,7 @@ hipError_t launch_bf16(const void* Q, const void* K, const void* V, void* O, flo
 template <int D, bool CAUSAL, int MODE>
 hipError_t launch_f32(const void* Q, const void* K, const void* V, void* O, float* L, int64_t BH,
                       int64_t N, float scale, fa355::ModeArgs sa, hipStream_t stream) {
-  constexpr int kRows = D >= 64 ? 64 / (D / 64) : 64;  // 16 rows at d = 256
+  constexpr int kRows = fa355::kF32Rows;  // query rows per workgroup
   const int num_qtiles = (int)((N + kRows - 1) / kRows);
   const int total = (int)(BH * num_qtiles * sa.num_splits);
   hipLaunchKernelGGL((fa355::fa_fwd_f32_kernel<D, CAUSAL, MODE>), dim3(total), dim3(64), 0,

@@ -1,9 +1,13 @@
 // Attention forward in float32 end to end (inputs, arithmetic, output).
 //
 // The same one-pass recurrence as the bf16 kernel (wmrh.cn FlashAttention
-// article, section 2.2), on the vector ALU: one wave per workgroup, one query
-// row per lane (two lanes per row when d = 128, each holding 64 of the d
-// components), 32-key tiles of K and V staged in LDS and read as broadcasts.
+// article, section 2.2), on the vector ALU: one wave per workgroup, four lanes
+// per query row (each holding a quarter of the d components, the dot products
+// completed with two lane exchanges), so 16 rows per workgroup; 32-key tiles
+// of K and V staged in LDS and read as broadcasts.  Four lanes per row rather
+// than one keep each lane's dependent chain of FMAs short: with one row per
+// lane a small launch (B = H = 1, N = 256) ran four single-wave workgroups
+// whose serial dot products set its time.
 // This is the exact-precision variant; bf16 inputs take the MFMA kernel.
 // In kSplit mode the workgroup covers the key range of one split and writes
 // the partial result described at ModeArgs (fa_common.hpp) instead of O, L;
@@ -18,6 +22,10 @@ namespace FA355_NS {
 // Keys per staged tile: 32, or 16 at d = 256 (two f32 tiles of 16 KB each).
 template <int D>
 constexpr int kF32Keys = D > 128 ? 16 : 32;
+// Lanes per query row and query rows per workgroup (the host sizes its grid
+// with kF32Rows).
+constexpr int kF32LanesPerRow = 4;
+constexpr int kF32Rows = 64 / kF32LanesPerRow;
 
 template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
@@ -28,14 +36,15 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(
   constexpr int kKeys = kF32Keys<D>;
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool SPARSE = MODE == kSparse;
-  constexpr int kLanesPerRow = D >= 64 ? D / 64 : 1;
-  constexpr int kRows = 64 / kLanesPerRow;  // query rows per workgroup
+  constexpr int kLanesPerRow = kF32LanesPerRow;
+  constexpr int kRows = kF32Rows;           // query rows per workgroup
   constexpr int kDl = D / kLanesPerRow;     // components of d held per lane
+  static_assert(kDl % 4 == 0, "whole float4 pieces per lane");
   __shared__ f32x4 ks[kKeys][D / 4];
   __shared__ f32x4 vs[kKeys][D / 4];
 
   const int lane = threadIdx.x;
-  const int part = lane / kRows;  // which 64 components of d (0 when d = 64)
+  const int part = lane / kRows;  // which quarter of the d components
   int split = 0, wg = blockIdx.x;
   if (SPLIT) {
     split = wg % split_args.num_splits;
