@@ -686,8 +686,9 @@ fa_fwd_bf16_kernel(
     // of exponentials of block 0, their sum.
     // Stage 2 (17 steps): eight pairs of exponentials of block 1, the row sum
     // into l_run, eight pairs of bf16 conversions into the P^T operands (whose
-    // rounded values are summed into lh_run during that tile's P V MFMAs,
-    // lh_step below).  L takes the sum of the float32 probabilities (l_run):
+    // rounded values are summed into lh_run: right after each conversion at
+    // d >= 128, under that tile's P V MFMAs at d <= 64, lh_step below).  L
+    // takes the sum of the float32 probabilities (l_run):
     // the sum of their bf16 roundings would move L by up to 2^-8 on rows with
     // few keys.  O is divided by the sum of the rounded values (lh_run), the
     // weights the P V MFMAs actually applied, so that O is their convex
