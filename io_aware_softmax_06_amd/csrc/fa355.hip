@@ -89,11 +89,14 @@ uint64_t split_workspace_bytes(uint64_t rows, int64_t d, int splits) {
 // instance's limit once per process (device-independent attribute).
 // Dynamic LDS of a bf16 launch: the K and V rings, plus on the block-sparse
 // path the tile list (one word per key block) and one count per wave.
+// Dense and persistent launches also hold the output staging area past the
+// rings.
 template <int D, int MODE>
 int64_t bf16_lds_bytes(int64_t N) {
-  int64_t bytes = fa355::Bf16Layout<D>::kBytes;
-  if (MODE == fa355::kSparse) bytes += 4 * ((N + fa355::kMaskBlock - 1) / fa355::kMaskBlock + fa355::kWaves);
-  return bytes;
+  using Lay = fa355::Bf16Layout<D>;
+  if (MODE == fa355::kSparse)
+    return Lay::kBytes + 4 * ((N + fa355::kMaskBlock - 1) / fa355::kMaskBlock + fa355::kWaves);
+  return MODE == fa355::kSplit ? Lay::kBytes : Lay::kBytesStaged;
 }
 
 // The bf16 kernels use more than the default 64 KB of dynamic LDS; raise each
@@ -104,7 +107,7 @@ hipError_t prepare_bf16() {
   static const hipError_t status = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&fa355::fa_fwd_bf16_kernel<D, CAUSAL, MODE, T>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
-      MODE == fa355::kSparse ? kMaxLds : fa355::Bf16Layout<D>::kBytes);
+      MODE == fa355::kSparse ? kMaxLds : (int)bf16_lds_bytes<D, MODE>(0));
   return status;
 }
 

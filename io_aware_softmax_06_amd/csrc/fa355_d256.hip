@@ -9,6 +9,8 @@
 #define FA355_BF16_VSTAGES 2
 #define FA355_BF16_OCCUPANCY 1
 
+// O is staged in the ring memory after the last loads (no LDS to spare).
+#define FA355_STAGE_DEDICATED 0
 #include "fa_fwd_bf16.hpp"
 #include "fa355_d256.h"
 

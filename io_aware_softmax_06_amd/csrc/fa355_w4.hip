@@ -12,6 +12,9 @@
 #define FA355_BF16_STAGES 3
 #define FA355_BF16_VSTAGES 2
 #define FA355_BF16_OCCUPANCY 2
+// O is staged in the ring memory after the last loads, keeping two
+// workgroups per CU.
+#define FA355_STAGE_DEDICATED 0
 
 #include "fa_fwd_bf16.hpp"
 #include "fa355_w4.h"

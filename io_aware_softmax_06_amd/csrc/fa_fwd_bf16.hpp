@@ -66,6 +66,12 @@ namespace FA355_NS {
 #ifndef FA355_BF16_VSTAGES
 #define FA355_BF16_VSTAGES FA355_BF16_STAGES
 #endif
+// 1: the output staging area of every wave sits past the K and V rings (the
+// 8-wave build: 160 KB of LDS at d = 128); 0: it reuses the ring memory after
+// the last loads (builds that must stay within a smaller LDS footprint).
+#ifndef FA355_STAGE_DEDICATED
+#define FA355_STAGE_DEDICATED 1
+#endif
 // Waves of one workgroup per SIMD that the register allocation must allow:
 // 2 for the 8-wave workgroups (two per SIMD); 1 when a 4-wave workgroup
 // fills the LDS alone (d = 256), which leaves it 512 registers per lane.
@@ -103,6 +109,18 @@ struct Bf16Layout {
   static constexpr int kOffV = kStages * kTileBytes;  // kVStages V tiles
   static constexpr int kBytes = (kStages + kVStages) * kTileBytes;  // 16 KB per slot at d = 128
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
+  // Output staging: each wave turns its 32 x D tile of O from column layout
+  // (one query per lane) into whole rows in LDS, so that the stores write
+  // complete rows.  Rows of D * 2 bytes, 16-byte chunks XOR-swizzled by the
+  // row.  Dedicated builds keep the staging area past the rings (no barrier,
+  // and the rings may hold the next query tile's first K and V tiles);
+  // otherwise it reuses the ring memory once every load has landed.
+  static constexpr int kStageRow = D * 2;
+  static constexpr int kStageWave = 32 * kStageRow;
+  static constexpr int kStageOff = FA355_STAGE_DEDICATED ? kBytes : 0;
+  static constexpr int kBytesStaged = FA355_STAGE_DEDICATED ? kBytes + kWaves * kStageWave : kBytes;
+  static_assert(kBytesStaged <= 160 * 1024 && kWaves * kStageWave <= kBytes + (kBytesStaged - kBytes),
+                "LDS for the output staging");
   static constexpr int kLoadsPerTile = kTileBytes / 1024;  // 1 KB per wave-wide direct load
   // Loads per wave; at d = 32 a tile is 4 KB, fewer pieces than waves, and
   // only the first kLoadsPerTile waves load (one piece each).
@@ -274,22 +292,32 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T
   using V8 = typename Elem<T>::v8;
   using Ops = ScoreOps<D, kAheadMax>;
   constexpr int kMfmas = Ops::kMfmas, kAhead = Ops::kAhead, kSlots = Ops::kSlots;
+  static_assert(kMfmas % 2 == 0 && kAhead % 2 == 0, "operands are read two MFMAs at a time");
   if constexpr (!PRE)
     static_for<kAhead>([&](auto ic) { ops.template issue<decltype(ic)::value>(kaddr); });
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
-  static_for<kMfmas>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    if constexpr (i + kAhead < kMfmas) {
-      ops.template issue<i + kAhead>(kaddr);
-      lds_wait<kAhead>();
-    } else {
-      lds_wait<kMfmas - 1 - i>();
-    }
-    pin(ops.a[i % kSlots]);
-    sacc[i % 2] = Elem<T>::mfma(__builtin_bit_cast(V8, ops.a[i % kSlots]), qf[i / 2], sacc[i % 2]);
-    work(ic);
-    __builtin_amdgcn_sched_barrier(0);
+  // MFMAs in pairs: one wait covers the operands of both.  The read kAhead
+  // MFMAs ahead of each MFMA is issued right before it, so that a read (not a
+  // VALU instruction) precedes every MFMA and the previous chunk's
+  // transcendental results need no wait states in between.
+  static_for<kMfmas / 2>([&](auto jc) {
+    constexpr int i0 = 2 * decltype(jc)::value;
+    static_for<2>([&](auto hc) {
+      constexpr int i = i0 + decltype(hc)::value;
+      if constexpr (i + kAhead < kMfmas) ops.template issue<i + kAhead>(kaddr);
+      if constexpr (i == i0) {
+        // outstanding: the reads of MFMAs i0 .. min(i0 + kAhead, kMfmas - 1)
+        constexpr int kLast = i0 + kAhead < kMfmas ? i0 + kAhead : kMfmas - 1;
+        lds_wait<(kLast - i0 - 1 > 0 ? kLast - i0 - 1 : 0)>();
+        pin(ops.a[i0 % kSlots]);
+        pin(ops.a[(i0 + 1) % kSlots]);
+      }
+      sacc[i % 2] =
+          Elem<T>::mfma(__builtin_bit_cast(V8, ops.a[i % kSlots]), qf[i / 2], sacc[i % 2]);
+      work(std::integral_constant<int, i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   });
 }
 
@@ -317,14 +345,6 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const typename Elem<T>::
   constexpr int kMfmas = (kBN / 16) * kBlocks;  // MFMA i: step i / kBlocks, block i % kBlocks
   constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
   constexpr int kSlots = kAhead + 2;            // a slot is refilled two MFMAs after its use
-  // Extra reads issued after the reads of MFMA i (in the chunks i - kAhead ..
-  // i - 1, from kExtraFrom on): they are younger, so a wait for MFMA i's
-  // operands allows that many more outstanding operations.
-  auto extras = [](auto ic) constexpr {
-    constexpr int i = decltype(ic)::value;
-    constexpr int lo = (i - kAhead > kExtraFrom ? i - kAhead : kExtraFrom);
-    return i - lo > 0 ? i - lo : 0;
-  };
   u32x2 v[kSlots][2];
   auto issue = [&](auto ic) {
     constexpr int i = decltype(ic)::value;
@@ -333,25 +353,43 @@ __device__ __forceinline__ void pv_tile(uint32_t vaddr, const typename Elem<T>::
     v[i % kSlots][0] = lds_tr16<off>(vaddr);
     v[i % kSlots][1] = lds_tr16<off + 4 * 64>(vaddr);
   };
+  static_assert(kMfmas % 2 == 0 && kAhead % 2 == 0, "operands are read two MFMAs at a time");
   static_for<kAhead>(issue);
-  static_for<kMfmas>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    constexpr int s = i / kBlocks, db = i % kBlocks;
-    constexpr int kX = extras(ic);
-    static_assert(2 * kAhead + kX <= 15, "lgkmcnt holds at most 15");
-    if constexpr (i + kAhead < kMfmas) {
-      issue(std::integral_constant<int, i + kAhead>{});
-      lds_wait<2 * kAhead + kX>();
-    } else {
-      lds_wait<2 * (kMfmas - 1 - i) + kX>();
-    }
-    u32x2(&cur)[2] = v[i % kSlots];
-    pin(cur[0]);
-    pin(cur[1]);
-    const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
-    oacc[db] = Elem<T>::mfma(__builtin_bit_cast(V8, a), pf[s], oacc[db]);
-    work(ic);
-    __builtin_amdgcn_sched_barrier(0);
+  // MFMAs in pairs, as in score_tile: one wait covers the operands of both,
+  // and the reads kAhead MFMAs ahead of each MFMA are issued right before it.
+  // Outstanding at the wait before MFMA i0: the reads of MFMAs i0 ..
+  // min(i0 + kAhead, kMfmas - 1), plus the extras issued since the reads of
+  // MFMA i0 + 1, which went out right before MFMA i0 + 1 - kAhead (or before
+  // MFMA 0): those of the chunks of MFMAs i0 + 1 - kAhead .. i0 - 1 that come
+  // from kExtraFrom on (the chunk of MFMA i0 runs after the wait).
+  auto extras_before = [](auto ic) constexpr {
+    constexpr int i0 = decltype(ic)::value;
+    constexpr int lo = (i0 + 1 - kAhead > kExtraFrom ? i0 + 1 - kAhead : kExtraFrom);
+    return i0 - lo > 0 ? i0 - lo : 0;
+  };
+  static_for<kMfmas / 2>([&](auto jc) {
+    constexpr int i0 = 2 * decltype(jc)::value;
+    static_for<2>([&](auto hc) {
+      constexpr int i = i0 + decltype(hc)::value;
+      constexpr int s = i / kBlocks, db = i % kBlocks;
+      if constexpr (i + kAhead < kMfmas) issue(std::integral_constant<int, i + kAhead>{});
+      if constexpr (i == i0) {
+        constexpr int kLast = i0 + kAhead < kMfmas ? i0 + kAhead : kMfmas - 1;
+        constexpr int kX = extras_before(std::integral_constant<int, i0>{});
+        constexpr int kN = 2 * (kLast - i0 - 1 > 0 ? kLast - i0 - 1 : 0) + kX;
+        static_assert(kN <= 15, "lgkmcnt holds at most 15");
+        lds_wait<kN>();
+        pin(v[i0 % kSlots][0]);
+        pin(v[i0 % kSlots][1]);
+        pin(v[(i0 + 1) % kSlots][0]);
+        pin(v[(i0 + 1) % kSlots][1]);
+      }
+      u32x2(&cur)[2] = v[i % kSlots];
+      const u32x4 a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
+      oacc[db] = Elem<T>::mfma(__builtin_bit_cast(V8, a), pf[s], oacc[db]);
+      work(std::integral_constant<int, i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   });
 }
 
@@ -464,10 +502,23 @@ fa_fwd_bf16_kernel(
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
   constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)
   constexpr bool kLhInPv = D <= 64;                 // where the rounded-P sum is taken (lh_step)
+  // 16-bit outputs go through the LDS staging area: with a dedicated area
+  // always (not the block-sparse path, whose tile list sits past the rings),
+  // otherwise in launches that are not persistent (the ring is free at the
+  // end).  The split path writes float32 partials directly.
+  constexpr bool kStagedStore =
+      !SPLIT && (FA355_STAGE_DEDICATED ? !SPARSE : !PERSIST);
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // The wave index as a scalar: everything derived from it (row ranges, tile
+  // counts, load destinations) stays in scalar registers and branches on it
+  // are uniform.
+  const int wave = tid >> 6;
+  // The same as a scalar, for the load destinations (LDS addresses are set
+  // through M0, a scalar register).
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int qi = lane & 31;  // query column of this lane inside the wave's 32
   const int hh = lane >> 5;  // half-wave
 
@@ -604,6 +655,14 @@ fa_fwd_bf16_kernel(
       my_tiles = wq0 < N ? total : 0;
     }
     const int last = n_tiles - 1;
+    // Leading tiles of the range that every row of the workgroup sees whole:
+    // inside N and, under the causal mask, before the workgroup's first row.
+    int n_safe = 0;
+    if constexpr (!SPARSE) {
+      int safe_end = min(kv_end, N & ~(kBN - 1));
+      if (CAUSAL) safe_end = min(safe_end, q0);
+      n_safe = safe_end > kv_lo ? (safe_end - kv_lo) / kBN : 0;
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -650,13 +709,23 @@ fa_fwd_bf16_kernel(
     auto entry_seen = [&](uint32_t e) { return !SPARSE || ((e >> (24 + (wave >> 1))) & 1u) != 0; };
     auto load_k = [&](int slot, uint32_t e) {
       load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes,
-                          PERSIST && (e & kNextTile) ? k_rsrc_next : k_rsrc, entry_kv0(e), wave,
+                          PERSIST && (e & kNextTile) ? k_rsrc_next : k_rsrc, entry_kv0(e), wave_s,
                           k_off);
     };
     auto load_v = [&](int slot, uint32_t e) {
       load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes,
-                          PERSIST && (e & kNextTile) ? v_rsrc_next : v_rsrc, entry_kv0(e), wave,
+                          PERSIST && (e & kNextTile) ? v_rsrc_next : v_rsrc, entry_kv0(e), wave_s,
                           v_off);
+    };
+
+    // The same for a key tile of this query tile's own range (no flag to test).
+    auto load_k_own = [&](int slot, uint32_t tile) {
+      load_tile_direct<D>(smem, Lay::kOffK + slot * Lay::kTileBytes, k_rsrc, (int)tile * kBN,
+                          wave_s, k_off);
+    };
+    auto load_v_own = [&](int slot, uint32_t tile) {
+      load_tile_direct<D>(smem, Lay::kOffV + slot * Lay::kTileBytes, v_rsrc, (int)tile * kBN,
+                          wave_s, v_off);
     };
 
     // Softmax of one tile's raw scores s, in two halves.  Stage 1: mask, row
@@ -909,26 +978,45 @@ fa_fwd_bf16_kernel(
       // a 2-deep V ring the V load goes first, so that it has the whole
       // iteration to land.
       constexpr bool kShortV = kVStages == 2;
-      auto refill_v = [&](int sk, int svs, uint32_t ev) {
-        if constexpr (kShortV) load_v(svs ^ 1, ev);
-        else load_v(wrap(sk + kStages - 1), ev);
+      auto refill_v = [&](auto checked_c, int sk, int svs, uint32_t ev) {
+        const int slot = kShortV ? svs ^ 1 : wrap(sk + kStages - 1);
+        if constexpr (decltype(checked_c)::value) load_v(slot, ev);
+        else load_v_own(slot, ev);
       };
-      auto iteration = [&](int t, int sk, int svs, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+      auto refill_k = [&](auto checked_c, int sk, uint32_t ek) {
+        if constexpr (decltype(checked_c)::value) load_k(wrap(sk + 1), ek);
+        else load_k_own(wrap(sk + 1), ek);
+      };
+      // CHECKED false: an iteration whose tiles need no checks, i.e. tile t+1
+      // is seen whole by every row of the workgroup (no mask, every wave
+      // has it) and the refills name tiles of this query tile's own range.
+      auto iteration = [&](auto checked_c, int t, int sk, int svs, f32x16(&cur)[2],
+                           f32x16(&nxt)[2]) {
+        constexpr bool CHECKED = decltype(checked_c)::value;
         // Entries of this iteration: tile t+1 (masked now), the K tile
         // t+1+kStages and the V tile (t+1 or t-1+kStages) loaded now.  On the
         // block-sparse path they are read here, before any operand read of the
         // iteration is in flight.
-        const bool boundary = PERSIST && has_next && t == last;
-        uint32_t e_next = entry(t + 1), e_k = entry(t + 1 + kStages);
-        uint32_t e_v = kShortV ? e_next : entry(t - 1 + kStages);
-        if constexpr (SPARSE) {
-          lds_wait<0>();
-          pin_entry(e_next);
-          pin_entry(e_k);
-          pin_entry(e_v);
+        const bool boundary = CHECKED && PERSIST && has_next && t == last;
+        uint32_t e_next, e_k, e_v;
+        if constexpr (CHECKED) {
+          e_next = entry(t + 1);
+          e_k = entry(t + 1 + kStages);
+          e_v = kShortV ? e_next : entry(t - 1 + kStages);
+          if constexpr (SPARSE) {
+            lds_wait<0>();
+            pin_entry(e_next);
+            pin_entry(e_k);
+            pin_entry(e_v);
+          }
+        } else {
+          const uint32_t e_t = (uint32_t)(kv_lo / kBN + t);
+          e_next = e_t + 1;
+          e_k = e_t + 1 + kStages;
+          e_v = kShortV ? e_next : e_t - 1 + kStages;
         }
-        if (t + 1 < my_tiles) {
-          mask_tile(e_next, cur);
+        if (!CHECKED || t + 1 < my_tiles) {
+          if constexpr (CHECKED) mask_tile(e_next, cur);
           // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
           // the V and K loads of later tiles issued early and in the middle.
           SoftmaxState st;
@@ -943,9 +1031,9 @@ fa_fwd_bf16_kernel(
                       [&](auto sic) { stage1_step(sic, cur, st); });
             run_steps(ic, std::integral_constant<int, kLhSteps>{},
                       [&](auto sic) { lh_step(sic, pf); });
-            if constexpr (kShortV && c == 0) refill_v(sk, svs, e_v);
-            if constexpr (!kShortV && c == 2) refill_v(sk, svs, e_v);
-            if constexpr (c == kMf / 2) load_k(wrap(sk + 1), e_k);
+            if constexpr (kShortV && c == 0) refill_v(checked_c, sk, svs, e_v);
+            if constexpr (!kShortV && c == 2) refill_v(checked_c, sk, svs, e_v);
+            if constexpr (c == kMf / 2) refill_k(checked_c, sk, e_k);
             if constexpr (kPre > 0 && c >= kMf - kPre)
               sops.template issue<c - (kMf - kPre)>(k_next);
           });
@@ -965,17 +1053,17 @@ fa_fwd_bf16_kernel(
           });
           pin_probs(pf);
         } else {
-          if constexpr (kShortV) refill_v(sk, svs, e_v);
+          if constexpr (kShortV) refill_v(checked_c, sk, svs, e_v);
           // Persistent, last tile with a next query tile: K_{t+1+S} is that
           // tile's K_S, and its slot still holds the next tile's K_0, unread.
           // The next prologue issues it after its first scores, as every
           // prologue does.
-          if (!(PERSIST && boundary)) load_k(wrap(sk + 1), e_k);
+          if (!(PERSIST && boundary)) refill_k(checked_c, sk, e_k);
           if (t < my_tiles) {
             pv_tile<D, T>(v_addr(svs), pf, oacc);
             static_for<kLhSteps>([&](auto sic) { lh_step(sic, pf); });
           }
-          if constexpr (!kShortV) refill_v(sk, svs, e_v);
+          if constexpr (!kShortV) refill_v(checked_c, sk, svs, e_v);
         }
 
         // K_{t+3} and V_{t+1} must have landed for every wave before anyone
@@ -991,13 +1079,24 @@ fa_fwd_bf16_kernel(
 
       // Two tiles per trip so that the two score buffers swap roles instead of
       // being copied (and, with a 2-deep V ring, V slots are constants).
+      // Iterations t < t_plain need no checks: tile t+1 is among the n_safe
+      // leading tiles that every row of the workgroup sees whole, and the
+      // refill K_{t+1+kStages} is still a tile of this range.
+      constexpr std::false_type kPlain{};
+      constexpr std::true_type kChecked{};
+      const int t_plain = max(0, min(n_safe - 1, last - kStages));
       int t = 0, sk = ring;
-      for (; t + 1 < n_tiles; t += 2) {
-        iteration(t, sk, kShortV ? 0 : sk, sB, sA);
-        iteration(t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
+      for (; t + 1 < t_plain; t += 2) {
+        iteration(kPlain, t, sk, kShortV ? 0 : sk, sB, sA);
+        iteration(kPlain, t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
         sk = wrap(sk + 2);
       }
-      if (t < n_tiles) iteration(t, sk, kShortV ? 0 : sk, sB, sA);
+      for (; t + 1 < n_tiles; t += 2) {
+        iteration(kChecked, t, sk, kShortV ? 0 : sk, sB, sA);
+        iteration(kChecked, t + 1, wrap(sk + 1), kShortV ? 1 : wrap(sk + 1), sA, sB);
+        sk = wrap(sk + 2);
+      }
+      if (t < n_tiles) iteration(kChecked, t, sk, kShortV ? 0 : sk, sB, sA);
       // The ring's last refills (clamped repeats of the last tile) are still in
       // flight; let them land before the workgroup can end and its LDS be reused.
       // Persistent with a next query tile: they are that tile's first loads.
@@ -1030,7 +1129,7 @@ fa_fwd_bf16_kernel(
             *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) = o4;
           }
         if (hh == 0) split_args.lpart[prow] = lse;
-      } else {
+      } else if constexpr (!kStagedStore) {
         uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -1042,7 +1141,63 @@ fa_fwd_bf16_kernel(
             *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hh) =
                 __builtin_bit_cast(u32x2, o4);
           }
-        if (hh == 0) Lse[(size_t)bh * N + qrow] = lse;
+      }
+      if (!SPLIT && hh == 0) Lse[(size_t)bh * N + qrow] = lse;
+    }
+    if constexpr (kStagedStore) {
+      // O through the wave's LDS staging area: the lane of query column qi
+      // writes its 8-byte pieces of row qi, then every lane reads 16
+      // consecutive bytes of a row and the wave stores 1 KB of consecutive
+      // rows per instruction.  The area is this wave's alone, and LDS
+      // operations of one wave complete in order.  The swizzle moves a row's
+      // 16-byte chunk c to c ^ (row & kSwz); it only changes address bits
+      // 4..8, above which the row and the wave's area start (the dynamic LDS
+      // of this kernel starts at address 0), so every address is one lane
+      // base XOR a constant.  The bases are pinned here: computed once
+      // outside the persistent loop, the 24 addresses would be held in
+      // registers across it.
+      using Lay2 = Bf16Layout<D>;
+      constexpr int kRowB = Lay2::kStageRow, kChunks = kRowB / 16;
+      constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
+      constexpr int kRowsPerRead = 1024 / kRowB;  // rows per 1 KB read
+      static_assert(kRowB % 64 == 0 && Lay2::kStageWave % 2048 == 0 &&
+                        Lay2::kStageOff % 2048 == 0, "staging address bits");
+      if constexpr (!FA355_STAGE_DEDICATED) {
+        // the ring memory: every wave's loads have landed (the loop's end
+        // waited for them) once all waves are here
+        block_sync();
+      }
+      const uint32_t wave_area = smem_lds + Lay2::kStageOff + wave * Lay2::kStageWave;
+      uint32_t wbase = wave_area + qi * kRowB + ((qi & kSwz) << 4) + 8 * hh;
+      const int r0 = lane * 16 / kRowB, c0 = lane * 16 % kRowB / 16;
+      uint32_t rbase = wave_area + r0 * kRowB + ((c0 ^ (r0 & kSwz)) << 4);
+      asm volatile("" : "+v"(wbase), "+v"(rbase));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          T o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = (T)(oacc[db][4 * g + r] * inv);
+          const int chunk = 4 * db + g;  // 16-byte chunk of d = 32db + 8g .. +7
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              (uintptr_t)(wbase ^ (uint32_t)(chunk << 4))) = __builtin_bit_cast(u32x2, o4);
+        }
+      // All reads first, then the stores, through a resource spanning this
+      // head's N rows: the range check drops the rows past N.
+      constexpr int kReads = 32 * kRowB / 1024;
+      u32x4 rows_out[kReads];
+#pragma unroll
+      for (int i = 0; i < kReads; ++i) {
+        const uint32_t a = (rbase ^ (uint32_t)(((i * kRowsPerRead) & kSwz) << 4)) + i * 1024;
+        rows_out[i] =
+            *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)a);
+      }
+      const __amdgpu_buffer_rsrc_t o_rsrc = head_resource(O + head, N * D * 2);
+#pragma unroll
+      for (int i = 0; i < kReads; ++i) {
+        const uint32_t off = (uint32_t)(wq0 + i * kRowsPerRead + r0) * (uint32_t)kRowB + c0 * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(rows_out[i], o_rsrc, off, 0, 0);
       }
     }
     if (!PERSIST || !has_next) break;
