@@ -48,7 +48,9 @@ typedef enum {
   FA_ERR_HIP = -8,            /* the HIP runtime reported an error at launch */
   FA_ERR_ARG = -9,            /* causal is not 0 or 1 */
   FA_ERR_SPLITS = -10,        /* num_splits is not in [1, 128] */
-  FA_ERR_WORKSPACE = -11      /* workspace NULL, too small or not 256-byte aligned */
+  FA_ERR_WORKSPACE = -11,     /* workspace NULL, too small or not 256-byte aligned */
+  FA_ERR_SCRATCH = -12        /* fa_fwd_splitkv_noalloc: the call needs more than
+                                 FA_NOALLOC_SCRATCH_BYTES of split workspace */
 } fa_status;
 
 /*
@@ -139,6 +141,32 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    int64_t B, int64_t H, int64_t N, int64_t d,
                    float scale, int causal, void* stream, int dtype,
                    int num_splits, void* workspace, int64_t workspace_bytes);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, result and errors are fa_fwd_splitkv's without `workspace` and
+ * `workspace_bytes`.  The partials go to a scratch buffer inside the library
+ * (a static device array of FA_NOALLOC_SCRATCH_BYTES, one per device, held
+ * until the process ends); the call allocates and frees nothing.  A call
+ * needing more than FA_NOALLOC_SCRATCH_BYTES, i.e.
+ * fa_fwd_splitkv_workspace(B, H, N, d, num_splits) > FA_NOALLOC_SCRATCH_BYTES,
+ * returns FA_ERR_SCRATCH before any HIP call.  Every element of the scratch
+ * that a call reads it has written first, so nothing is cleared and the
+ * contents left by an earlier call do not matter.
+ *
+ * All calls on one device share that device's buffer: two calls that may run
+ * at the same time on one device (different streams without ordering) race
+ * on it and give undefined results.  Order them (one stream, or events).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* L,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, int causal, void* stream, int dtype,
+                           int num_splits);
 
 /*
  * fa_fwd_blocksparse -- fa_fwd restricted to the key blocks a block mask

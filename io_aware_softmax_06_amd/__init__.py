@@ -52,6 +52,9 @@ FA_ERR_HIP = -8
 FA_ERR_ARG = -9
 FA_ERR_SPLITS = -10
 FA_ERR_WORKSPACE = -11
+FA_ERR_SCRATCH = -12
+# Size of the library's own split workspace (fa_fwd_splitkv_noalloc).
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _lib = None
 
@@ -84,6 +87,10 @@ def load(path=LIB_PATH):
                                    ctypes.c_float, ctypes.c_int, vp, ctypes.c_int,
                                    ctypes.c_int, vp, i64]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                           ctypes.c_float, ctypes.c_int, vp, ctypes.c_int,
+                                           ctypes.c_int]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                        ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, i64]
     lib.fa_fwd_blocksparse.restype = ctypes.c_int
@@ -115,6 +122,12 @@ def fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_
     """Direct call of the C entry point; returns its status code."""
     return load().fa_fwd_splitkv(Q, K, V, O, L, B, H, N, d, float(scale), int(causal), stream,
                                  dtype, int(num_splits), workspace, workspace_bytes)
+
+
+def fa_fwd_splitkv_noalloc(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_splits):
+    """Direct call of the C entry point; returns its status code."""
+    return load().fa_fwd_splitkv_noalloc(Q, K, V, O, L, B, H, N, d, float(scale), int(causal),
+                                         stream, dtype, int(num_splits))
 
 
 def fa_fwd_blocksparse(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, block_mask,
@@ -234,6 +247,25 @@ def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, out=None, lse=Non
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse, workspace
+
+
+def fwd_splitkv_noalloc(q, k, v, num_splits, scale=None, causal=False, out=None, lse=None,
+                        stream=None):
+    """Key-range split forward on the library's own scratch buffer; returns (O, L).
+
+    The library allocates nothing for the partials: they go to its fixed
+    per-device scratch of NOALLOC_SCRATCH_BYTES (FaError FA_ERR_SCRATCH when
+    the call needs more).  Calls that may overlap on one device race on it.
+    (O and L are still allocated here when not given.)
+    """
+    (B, H, N, d), scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
+    with _on_device(q.device):
+        rc = fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, N, d, scale, 1 if causal else 0,
+                                    stream.cuda_stream, _dtype_code(q), num_splits)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse
 
 
 def split_partials(workspace, num_splits, B, H, N, d):

@@ -10,6 +10,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_fwd_bf16.hpp"
 #include "fa_fwd_f32.hpp"
@@ -21,7 +22,7 @@
 
 namespace {
 
-constexpr int kVersion = 500;  // 0.5.0: fp16 inputs
+constexpr int kVersion = 600;  // 0.6.0: fa_fwd_splitkv_noalloc
 constexpr int kMaxSplits = 128;
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
@@ -282,10 +283,13 @@ extern "C" int64_t fa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int
   return (int64_t)bytes;
 }
 
-extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
-                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                              void* stream, int dtype, int num_splits, void* workspace,
-                              int64_t workspace_bytes) {
+namespace {
+
+// The split forward on a given workspace (fa_fwd_splitkv's checks and
+// launches); `workspace` is device memory of at least `workspace_bytes`.
+int splitkv_impl(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
+                 int64_t H, int64_t N, int64_t d, float scale, int causal, void* stream,
+                 int dtype, int num_splits, void* workspace, int64_t workspace_bytes) {
   Sizes sz;
   const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
   if (rc != FA_OK) return rc;
@@ -320,6 +324,59 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
       err = launch_merge_d<float>(opart, lpart, O, L, num_splits, sz.rows, d, s);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
+                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                              void* stream, int dtype, int num_splits, void* workspace,
+                              int64_t workspace_bytes) {
+  return splitkv_impl(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_splits,
+                      workspace, workspace_bytes);
+}
+
+// The library's own split workspace for callers that cannot allocate: one
+// copy per device, held while the process lives.  In host code this name is
+// a host-side stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device (resolved on the first
+// call on that device, with it current), or nullptr if that failed.
+void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) addr[dev] = p;
+  });
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                      float* L, int64_t B, int64_t H, int64_t N, int64_t d,
+                                      float scale, int causal, void* stream, int dtype,
+                                      int num_splits) {
+  // Sizes first, so that every rejection happens before any HIP call.
+  Sizes sz;
+  const int rc = check_args(Q, K, V, O, L, B, H, N, d, scale, causal, dtype, &sz);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  const uint64_t need = split_workspace_bytes(sz.rows, d, num_splits);
+  if (need == 0) return FA_ERR_SHAPE;
+  if (need > (uint64_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return FA_ERR_HIP;
+  return splitkv_impl(Q, K, V, O, L, B, H, N, d, scale, causal, stream, dtype, num_splits, ws,
+                      (int64_t)FA_NOALLOC_SCRATCH_BYTES);
 }
 
 extern "C" int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L,
@@ -521,6 +578,8 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_SPLITS: return "num_splits must be between 1 and 128";
     case FA_ERR_WORKSPACE: return "workspace is NULL, smaller than fa_fwd_splitkv_workspace() "
                                   "bytes or not 256-byte aligned";
+    case FA_ERR_SCRATCH: return "the split workspace this call needs exceeds the library's "
+                                "fixed scratch buffer (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status code";
   }
 }

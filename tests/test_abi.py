@@ -49,7 +49,8 @@ def test_version(lib):
 def test_strerror_covers_every_code(lib):
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED_D,
              fa.FA_ERR_DTYPE, fa.FA_ERR_SCALE, fa.FA_ERR_ALIGN, fa.FA_ERR_ALIAS,
-             fa.FA_ERR_HIP, fa.FA_ERR_ARG, fa.FA_ERR_SPLITS, fa.FA_ERR_WORKSPACE]
+             fa.FA_ERR_HIP, fa.FA_ERR_ARG, fa.FA_ERR_SPLITS, fa.FA_ERR_WORKSPACE,
+             fa.FA_ERR_SCRATCH]
     msgs = [fa.fa_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert fa.fa_strerror(12345) == "unknown status code"
@@ -193,6 +194,45 @@ def test_splitkv_bad_workspace(lib):
 @pytest.mark.parametrize("ws", [Q, K + 256, V - 256, O, L - 1024])
 def test_splitkv_workspace_alias(lib, ws):
     assert call_split(ws=ws) == fa.FA_ERR_ALIAS
+
+
+def call_noalloc(S=4, **over):
+    a = dict(GOOD, **over)
+    return fa.fa_fwd_splitkv_noalloc(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["H"],
+                                     a["N"], a["d"], a["scale"], a["causal"], a["stream"],
+                                     a["dtype"], S)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "fa355.h")).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "FA_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == fa.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED_D), (dict(dtype=5), fa.FA_ERR_DTYPE),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(causal=2), fa.FA_ERR_ARG),
+    (dict(O=O + 8), fa.FA_ERR_ALIGN), (dict(L=Q), fa.FA_ERR_ALIAS)])
+def test_noalloc_shares_fwd_checks(lib, over, code):
+    assert call_noalloc(**over) == code
+
+
+@pytest.mark.parametrize("S", [0, 129])
+def test_noalloc_bad_splits(lib, S):
+    assert call_noalloc(S=S) == fa.FA_ERR_SPLITS
+
+
+def test_noalloc_rejects_more_than_its_scratch(lib):
+    # The largest call that fits, and one row more: the partials are
+    # S * rows * (d + 1) * 4 bytes.  Rejected before any HIP call.
+    S, d = 4, 128
+    rows_fit = fa.NOALLOC_SCRATCH_BYTES // (S * (d + 1) * 4)
+    assert ws_bytes(1, 1, rows_fit, d, S) <= fa.NOALLOC_SCRATCH_BYTES
+    assert ws_bytes(1, 1, rows_fit + 1, d, S) > fa.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(S=S, B=1, H=1, N=rows_fit + 1, d=d) == fa.FA_ERR_SCRATCH
+    assert call_noalloc(S=128, B=2, H=3, N=4096, d=256) == fa.FA_ERR_SCRATCH
 
 
 def test_splitkv_grid_too_large(lib):
