@@ -40,6 +40,13 @@ struct Elem<__bf16> {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
   }
+  // The same with the pair index i (0..3) given at run time (unrolled loops).
+  static __device__ __forceinline__ float add_pair_rt(v8 x, int i, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 pair = {x[2 * i], x[2 * i + 1]};
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+  }
 };
 template <>
 struct Elem<_Float16> {
@@ -52,6 +59,12 @@ struct Elem<_Float16> {
   static __device__ __forceinline__ float add_pair(v8 x, float acc) {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     const f16x2 pair = {x[2 * I], x[2 * I + 1]};
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(pair, one, acc, false);
+  }
+  static __device__ __forceinline__ float add_pair_rt(v8 x, int i, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 pair = {x[2 * i], x[2 * i + 1]};
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(pair, one, acc, false);
   }

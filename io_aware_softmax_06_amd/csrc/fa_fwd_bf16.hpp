@@ -91,6 +91,10 @@ static_assert((kStages >= 3 && kVStages == kStages) || (kStages == 3 && kVStages
               "ring depths");
 static_assert(kWaves == 4 || kWaves == 8, "waves per workgroup");
 constexpr float kTau = 8.0f;   // allowed growth of a row maximum before rescaling (log2 units)
+// Score-operand reads issued this many MFMAs ahead of their use.
+#ifndef FA355_SCORE_AHEAD
+#define FA355_SCORE_AHEAD 4
+#endif
 #ifndef FA355_XPHASE
 #define FA355_XPHASE 1
 #endif
@@ -271,7 +275,7 @@ struct NoWork {
 // phase before it can issue the first kAhead reads early (the K tile is
 // already valid then): the first MFMAs of the score phase find their operands
 // in registers instead of waiting for LDS.
-template <int D, int kAheadMax = 6>
+template <int D, int kAheadMax = FA355_SCORE_AHEAD>
 struct ScoreOps {
   static constexpr int kMfmas = 2 * (D / 16);  // MFMA i: slab i / 2, block i % 2
   static constexpr int kAhead = kAheadMax < kMfmas ? kAheadMax : kMfmas;
@@ -285,7 +289,7 @@ struct ScoreOps {
 
 // PRE: the first kAhead reads were issued by the caller (ScoreOps::issue<0..
 // kAhead-1>, in order, with no LDS operation of its own after them).
-template <int D, typename T = __bf16, bool PRE = false, int kAheadMax = 6, typename Work = NoWork>
+template <int D, typename T = __bf16, bool PRE = false, int kAheadMax = FA355_SCORE_AHEAD, typename Work = NoWork>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
                                            f32x16 (&sacc)[2], ScoreOps<D, kAheadMax>& ops,
                                            Work&& work = Work{}) {
@@ -321,7 +325,7 @@ __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T
   });
 }
 
-template <int D, typename T = __bf16, int kAheadMax = 6, typename Work = NoWork>
+template <int D, typename T = __bf16, int kAheadMax = FA355_SCORE_AHEAD, typename Work = NoWork>
 __device__ __forceinline__ void score_tile(uint32_t kaddr, const typename Elem<T>::v8 (&qf)[D / 16],
                                            f32x16 (&sacc)[2], Work&& work = Work{}) {
   ScoreOps<D, kAheadMax> ops;
@@ -501,7 +505,7 @@ fa_fwd_bf16_kernel(
   using Lay = Bf16Layout<D>;
   constexpr int kVmPerTile = Lay::kLoadsPerWave;    // direct loads a wave issues per tile
   constexpr int kMf = D / 8;                        // MFMAs per stream per tile (16 at d = 128)
-  constexpr bool kLhInPv = D <= 64;                 // where the rounded-P sum is taken (lh_step)
+  constexpr bool kLhInPv = false;                   // where the rounded-P sum is taken (lh_step)
   // 16-bit outputs go through the LDS staging area: with a dedicated area
   // always (not the block-sparse path, whose tile list sits past the rings),
   // otherwise in launches that are not persistent (the ring is free at the
@@ -734,7 +738,8 @@ fa_fwd_bf16_kernel(
     // bf16 B operands of O^T += V^T P^T (16-key step s2 takes elements
     // 8(s2%2) .. 8(s2%2)+7 of block s2/2, i.e. keys 16 s2 + 8hh + (0..7)).
     // s element 4g+r of block kb is key kv0 + 32kb + key_of_row(8g + 4hh + r).
-    auto mask_tile = [&](uint32_t ent, f32x16(&sc)[2]) {
+    // Returns whether the tile needed a mask for this wave (uniform).
+    auto mask_tile = [&](uint32_t ent, f32x16(&sc)[2]) -> bool {
       const int kv0 = entry_kv0(ent);
       const bool hidden = !entry_seen(ent);  // a key block this wave's query block does not see
       const bool need_mask = hidden || (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
@@ -747,6 +752,7 @@ fa_fwd_bf16_kernel(
             if (hidden || key >= N || (CAUSAL && key > qrow)) sc[kb][e] = kNegInf;
           }
       }
+      return need_mask;
     };
     // The softmax of a tile as numbered steps, so that each MFMA of a phase can
     // be given its share (step s of NS goes after MFMA s * kMf / NS).
@@ -840,6 +846,91 @@ fa_fwd_bf16_kernel(
       if constexpr (k == 0) lh_run *= lh_alpha;
       lh_run = Elem<T>::template add_pair<p0>(pfo[s2], lh_run);
       lh_run = Elem<T>::template add_pair<p0 + 1>(pfo[s2], lh_run);
+    };
+    // The tile's softmax without its row maximum.  When the previous tile
+    // moved no reference point of the wave, the next tile's scores are
+    // exponentiated against the current reference right away: the row
+    // maximum, its half-wave exchange and the reference update are skipped.
+    // The raw scores are kept, and the tile's half-row sums of the
+    // probabilities are checked at the end: if one exceeds kFastLimit (some
+    // probability above it, which the reference rule would have moved), the
+    // tile is redone along the path with the maximum, and the wave returns to
+    // that path for the next tile.  Otherwise the result is the one the
+    // reference rule gives: the same reference, the same probabilities.
+    constexpr float kFastLimit = 65536.f;  // 2^16
+    struct FastState {
+      float l, lh;   // this tile's sums of the float32 and of the rounded probabilities
+      float tp[8][2];  // probabilities of pair k until their P^T step is free
+    };
+    // Pair k (0..15) of the tile: elements 2(k%8), 2(k%8)+1 of block k/8,
+    // i.e. elements j, j+1 (j = 2(k%4)) of P^T step k/4.  Phase 1 takes
+    // pairs 0..7 (steps 0, 1) under the P V MFMAs: the exponentials of pair
+    // k after MFMA k*kMf/8, its conversion once MFMA (k/4 + 1)*kBlocks - 1,
+    // the last to read the old step, has gone (kBlocks = D/32 MFMAs per
+    // step); phase 3 takes pairs 8..15 (steps 2, 3, free by then).
+    constexpr int kPvBlocks = D / 32;
+    auto fast_step = [&](auto ic, auto phase3_c, f32x16(&sc)[2], FastState& fs,
+                         V8(&pfo)[kBN / 16]) {
+      constexpr int c = decltype(ic)::value;
+      constexpr bool P3 = decltype(phase3_c)::value;
+      static_for<8>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;        // pair within the phase
+        constexpr int k = kk + (P3 ? 8 : 0);            // pair of the tile
+        constexpr int kb = k / 8, e = 2 * (k % 8);      // block and element
+        constexpr int s2 = k / 4, j = 2 * (k % 4);      // P^T step and element
+        constexpr int ce = kk * kMf / 8;                // chunk of the exponentials
+        constexpr int free_at = P3 ? 0 : (s2 + 1) * kPvBlocks - 1;
+        constexpr int cc0 = kMf >= 16 ? ce + 1 : ce;
+        constexpr int cc = cc0 > free_at ? cc0 : free_at;  // chunk of sum and conversion
+        if constexpr (c == ce) {
+          fs.tp[kk][0] = fast_exp2(__builtin_fmaf(sc[kb][e], scale_log2, -base_run));
+          fs.tp[kk][1] = fast_exp2(__builtin_fmaf(sc[kb][e + 1], scale_log2, -base_run));
+        }
+        if constexpr (c == cc) {
+          fs.l = (k == 0 ? fs.tp[kk][0] : fs.l + fs.tp[kk][0]) + fs.tp[kk][1];
+          pfo[s2][j] = (T)fs.tp[kk][0];
+          pfo[s2][j + 1] = (T)fs.tp[kk][1];
+          fs.lh = Elem<T>::template add_pair<j / 2>(pfo[s2], k == 0 ? 0.f : fs.lh);
+        }
+      });
+    };
+    // The tile again along the reference rule, for a wave whose check
+    // failed: row maximum, reference update, the output and both sums moved
+    // to the new reference, then every probability from the raw scores.  The
+    // arithmetic of each step is that of stages 1 and 2.
+    // Returns the factor that moves the output to the new reference point
+    // (1 when no row of the wave moved); the caller applies it.
+    auto redo_tile = [&](const f32x16(&sc)[2], V8(&pfo)[kBN / 16], bool& moved) -> float {
+      float m = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = (kb == 0 ? 2 : 0); e < 16; e += 2) m = fmaxf(fmaxf(m, sc[kb][e]), sc[kb][e + 1]);
+      const float mx = max_halves(m);
+      const float cand = mx * scale_log2;
+      const bool need = cand > base_run + kTau;
+      const float base_new = need ? cand : base_run;
+      const float alpha = fast_exp2(base_run - base_new);
+      m_ref = need ? mx : m_ref;
+      base_run = base_new;
+      moved = __builtin_amdgcn_ballot_w64(need) != 0;
+      float lsum = 0.f, lhs = lh_run * alpha;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int kb = k / 8, e = 2 * (k % 8), s2 = k / 4, j = 2 * (k % 4);
+        const float p0 = fast_exp2(__builtin_fmaf(sc[kb][e], scale_log2, -base_run));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[kb][e + 1], scale_log2, -base_run));
+        lsum += p0 + p1;
+        pfo[s2][j] = (T)p0;
+        pfo[s2][j + 1] = (T)p1;
+        lhs = Elem<T>::add_pair_rt(pfo[s2], j / 2, lhs);
+        // one pair at a time: all exponentials at once would need 32 more
+        // registers at a point where both score tiles are live
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run = __builtin_fmaf(l_run, alpha, lsum);
+      lh_run = lhs;
+      return alpha;
     };
     // Steps of a stage that belong after MFMA i of a kMf-MFMA phase.
     auto run_steps = [&](auto ic, auto nsteps_ic, auto&& step) {
@@ -949,6 +1040,8 @@ fa_fwd_bf16_kernel(
         pin(w);
         qf[s] = __builtin_bit_cast(V8, w);
       }
+      // The next plain tile may skip its row maximum (see FastState).
+      bool fast = false;
       if (my_tiles > 0) {
         score_tile<D, T>(k_addr(ring), qf, sA);
         score_tile<D, T>(k_addr(wrap(ring + 1)), qf, sB);
@@ -956,6 +1049,7 @@ fa_fwd_bf16_kernel(
         SoftmaxState st;
         stage1(sA, st);
         stage2(sA, st, pf);
+        fast = __builtin_amdgcn_ballot_w64(st.need) == 0;
       }
       uint32_t es = entry(kStages);
       if constexpr (SPARSE) {
@@ -1016,42 +1110,86 @@ fa_fwd_bf16_kernel(
           e_v = kShortV ? e_next : e_t - 1 + kStages;
         }
         if (!CHECKED || t + 1 < my_tiles) {
-          if constexpr (CHECKED) mask_tile(e_next, cur);
-          // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU), with
-          // the V and K loads of later tiles issued early and in the middle.
-          SoftmaxState st;
-          // The last MFMAs of this phase issue the first operand reads of the
+          // The softmax without maximum needs an unmasked tile (decided per
+          // wave, from its own rows, so that every launch shape and path
+          // takes the same decisions for a row and the results agree bitwise).
+          bool fast_now = fast;
+          if constexpr (CHECKED) {
+            const bool masked = mask_tile(e_next, cur);  // always applied
+            fast_now = fast && !masked;
+          }
+          // The last MFMAs of phase 1 issue the first operand reads of the
           // score phase (K_{t+2} has been valid since the last barrier).
           ScoreOps<D> sops;
           const uint32_t k_next = k_addr(wrap(sk + 2));
           constexpr int kPre = kXPhase ? ScoreOps<D>::kAhead : 0;
-          pv_tile<D, T, kMf - kPre>(v_addr(svs), pf, oacc, [&](auto ic) {
+          // Loads of later tiles (V early, K half way) and those score-phase
+          // reads, issued between the P V MFMAs.
+          auto pv_extras = [&](auto ic) {
             constexpr int c = decltype(ic)::value;
-            run_steps(ic, std::integral_constant<int, kStage1Steps>{},
-                      [&](auto sic) { stage1_step(sic, cur, st); });
-            run_steps(ic, std::integral_constant<int, kLhSteps>{},
-                      [&](auto sic) { lh_step(sic, pf); });
             if constexpr (kShortV && c == 0) refill_v(checked_c, sk, svs, e_v);
             if constexpr (!kShortV && c == 2) refill_v(checked_c, sk, svs, e_v);
             if constexpr (c == kMf / 2) refill_k(checked_c, sk, e_k);
             if constexpr (kPre > 0 && c >= kMf - kPre)
               sops.template issue<c - (kMf - kPre)>(k_next);
-          });
-          pin_scores(cur);
-          asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
-
-          // Phase 2: move the output to the new reference (rare).
-          if (__builtin_amdgcn_ballot_w64(st.need) != 0) {
+          };
+          if (fast_now) {
+            // Phase 1: P V of tile t under the first half of tile t+1's
+            // softmax without maximum; phase 3: scores of tile t+2 under the
+            // second half.  Then the check.
+            FastState fs;
+            pv_tile<D, T, kMf - kPre>(v_addr(svs), pf, oacc, [&](auto ic) {
+              fast_step(ic, std::false_type{}, cur, fs, pf);
+              pv_extras(ic);
+            });
+            score_tile<D, T, kXPhase>(k_next, qf, nxt, sops, [&](auto ic) {
+              fast_step(ic, std::true_type{}, cur, fs, pf);
+            });
+            bool moved = false;
+            float alpha = 1.f;
+            if (__builtin_amdgcn_ballot_w64(fs.l > kFastLimit) != 0) {
+              // Some probability is too large: the tile again, with the
+              // maximum (the raw scores are intact).
+              alpha = redo_tile(cur, pf, moved);
+              fast = false;
+            } else {
+              l_run += fs.l;
+              lh_run += fs.lh;
+            }
+            pin_probs(pf);
+            // the output moved to the new reference point (rare)
+            if (moved) {
 #pragma unroll
-            for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
-          }
+              for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+            }
+          } else {
+            // Phase 1: P V of tile t (MFMA) under stage 1 of tile t+1 (VALU).
+            SoftmaxState st;
+            pv_tile<D, T, kMf - kPre>(v_addr(svs), pf, oacc, [&](auto ic) {
+              run_steps(ic, std::integral_constant<int, kStage1Steps>{},
+                        [&](auto sic) { stage1_step(sic, cur, st); });
+              run_steps(ic, std::integral_constant<int, kLhSteps>{},
+                        [&](auto sic) { lh_step(sic, pf); });
+              pv_extras(ic);
+            });
+            pin_scores(cur);
+            asm volatile("" : "+v"(st.half_sum), "+v"(st.alpha));
 
-          // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU).
-          score_tile<D, T, kXPhase>(k_next, qf, nxt, sops, [&](auto ic) {
-            run_steps(ic, std::integral_constant<int, kStage2Steps>{},
-                      [&](auto sic) { stage2_step(sic, cur, st, pf); });
-          });
-          pin_probs(pf);
+            // Phase 2: move the output to the new reference (rare).
+            const bool moved = __builtin_amdgcn_ballot_w64(st.need) != 0;
+            if (moved) {
+#pragma unroll
+              for (int i = 0; i < D / 32; ++i) oacc[i] *= st.alpha;
+            }
+            fast = !moved;
+
+            // Phase 3: scores of tile t+2 (MFMA) under stage 2 of tile t+1 (VALU).
+            score_tile<D, T, kXPhase>(k_next, qf, nxt, sops, [&](auto ic) {
+              run_steps(ic, std::integral_constant<int, kStage2Steps>{},
+                        [&](auto sic) { stage2_step(sic, cur, st, pf); });
+            });
+            pin_probs(pf);
+          }
         } else {
           if constexpr (kShortV) refill_v(checked_c, sk, svs, e_v);
           // Persistent, last tile with a next query tile: K_{t+1+S} is that
@@ -1167,11 +1305,16 @@ fa_fwd_bf16_kernel(
         // waited for them) once all waves are here
         block_sync();
       }
-      const uint32_t wave_area = smem_lds + Lay2::kStageOff + wave * Lay2::kStageWave;
-      uint32_t wbase = wave_area + qi * kRowB + ((qi & kSwz) << 4) + 8 * hh;
-      const int r0 = lane * 16 / kRowB, c0 = lane * 16 % kRowB / 16;
-      uint32_t rbase = wave_area + r0 * kRowB + ((c0 ^ (r0 & kSwz)) << 4);
-      asm volatile("" : "+v"(wbase), "+v"(rbase));
+      // The lane index recomputed here (mbcnt, in a volatile asm that the
+      // compiler cannot hoist), so that nothing derived from it is held in
+      // registers across the loop.
+      int ll;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ll));
+      const int lq = ll & 31, lh = ll >> 5;
+      const uint32_t wave_area = smem_lds + Lay2::kStageOff + wave_s * Lay2::kStageWave;
+      const uint32_t wbase = wave_area + lq * kRowB + ((lq & kSwz) << 4) + 8 * lh;
+      const int r0 = ll * 16 / kRowB, c0 = ll * 16 % kRowB / 16;
+      const uint32_t rbase = wave_area + r0 * kRowB + ((c0 ^ (r0 & kSwz)) << 4);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
