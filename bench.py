@@ -109,6 +109,28 @@ def measured_traffic(workload_name):
         return None
 
 
+def host_description():
+    """The host CPU the oracle runs on: lscpu's model name, the logical CPUs
+    this process may run on, and the BLAS threads NumPy uses."""
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        model = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": blas}
+
+
 def cpu_baseline(w, seed, budget_s=10.0, block_mask=None, flops=None):
     """The float64 oracle on whole heads of the same inputs, ~budget_s seconds.
 
@@ -147,6 +169,7 @@ def cpu_baseline(w, seed, budget_s=10.0, block_mask=None, flops=None):
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, seed {seed}, "
                   f"float64 NumPy oracle with materialised S, {dt:.1f} s",
+        "host": host_description(),
     }
 
 
@@ -177,7 +200,8 @@ def cpu_baseline_backward(w, seed, budget_s=10.0):
     return {"value": round(per_head * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, seed {seed}, "
-                      f"float64 NumPy backward oracle with materialised S and P, {dt:.1f} s"}
+                      f"float64 NumPy backward oracle with materialised S and P, {dt:.1f} s",
+            "host": host_description()}
 
 
 def main():

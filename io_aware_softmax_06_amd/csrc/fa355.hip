@@ -499,7 +499,11 @@ extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) 
     return FA_ERR_SHAPE;
   if (B * H > INT_MAX) return FA_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;  // backward: d <= 128
-  return B * H * N * 4;
+  // B*H and N are each below 2^31, so the row count fits 62 bits; four bytes
+  // per row must still fit a signed 64-bit result.
+  const uint64_t rows = (uint64_t)(B * H) * (uint64_t)N;
+  if (rows > (uint64_t)INT64_MAX / 4) return FA_ERR_SHAPE;
+  return (int64_t)(rows * 4);
 }
 
 extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

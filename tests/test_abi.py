@@ -300,6 +300,17 @@ def test_bwd_workspace_size(lib):
     assert fa.fa_bwd_workspace(1, 1, 8, 96) == fa.FA_ERR_UNSUPPORTED_D
 
 
+def test_bwd_workspace_extreme_shape(lib):
+    # B*H near 2^31 and N near 2^31: about 2^62 rows, whose four bytes each
+    # would overflow a signed 64-bit size.
+    big = 2**31 - 257
+    assert fa.fa_bwd_workspace(1, 2**31 - 1, big, 64) == fa.FA_ERR_SHAPE
+    # just below the limit (about 2^61 rows) the size is exact and positive
+    rows = 2**30 * big
+    assert rows <= (2**63 - 1) // 4
+    assert fa.fa_bwd_workspace(2**15, 2**15, big, 64) == rows * 4
+
+
 @pytest.mark.parametrize("field", ["Q", "K", "V", "O", "L", "dO", "dQ", "dK", "dV"])
 def test_bwd_null(lib, field):
     assert call_bwd(**{field: None}) == fa.FA_ERR_NULL
