@@ -32,7 +32,12 @@ the default is K eager calls.
 Prints ONE JSON line.  `value` is attention TFLOP/s with the conventional
 count 4*B*H*N^2*d (halved for causal) over the timed steps' wall time.
 `roofline` relates the kernel's average launch duration (HIP events on the
-launch stream) to the dense bf16 MFMA peak.  `cpu_baseline` times the float64
+launch stream) to the dense bf16 MFMA peak, with the MFMA-busy fraction and
+HBM bytes of the committed counter summaries (null once the kernel sources
+have changed since they were taken) and, for d <= 64, the VALU-issue bound.
+`steady` times the same step again after the timed window, once at least 300
+launches have run: with a short --warmup the timed window falls in the GPU's
+slower first ~100 launches, and the two figures then differ.  `cpu_baseline` times the float64
 CPU oracle on a bounded sample of the same workload (whole heads, ~10 s).
 """
 
@@ -53,6 +58,9 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) + % of bf16 MFMA peak, 1×MI35
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_F32_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
+# Launches after which the GPU clock has settled (the slow start lasts about
+# 100 launches of the causal N=4096 workload, ~30 ms).
+STEADY_AFTER_LAUNCHES = 300
 CSRC = os.path.join(ROOT, "io_aware_softmax_06_amd", "csrc")
 
 
@@ -86,14 +94,11 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch from the committed PMC summary, if it is current.
-
-    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each
-    scaled by the copy-kernel calibration factor) and the digest of the kernel
-    sources it was taken with; a changed kernel makes the figure stale (None).
-    """
-    path = os.path.join(PROFILES, f"hbm_traffic_{workload_name}.txt")
+def committed_fields(kind, workload_name):
+    """The `name: value` fields of profiles/<kind>_<workload>.txt, or None when
+    the file is missing or was taken with other kernel sources (its
+    source_digest differs from the current one)."""
+    path = os.path.join(PROFILES, f"{kind}_{workload_name}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -103,8 +108,53 @@ def measured_traffic(workload_name):
             fields[m.group(1)] = m.group(2)
     if fields.get("source_digest") != kernel_source_digest():
         return None
+    return fields
+
+
+def measured_mfma_busy(workload_name):
+    """MFMA-busy fraction of the committed counter summary (None if stale):
+    SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles of the dispatch
+    (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)."""
+    f = committed_fields("mfma_busy", workload_name)
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return None if f is None else float(f["mfma_busy"])
+    except (KeyError, ValueError):
+        return None
+
+
+def valu_bound(workload_name, flops, peak):
+    """The VALU-issue bound of one launch from the committed counters (None if
+    stale).  The non-MFMA VALU instructions of the dispatch, spread evenly
+    over the 1024 SIMDs at the issue costs measured for this kernel's mix,
+    give `valu_us` at the 2.4 GHz peak clock; the MFMA work gives `mfma_us`.
+    A SIMD issues VALU work of one wave while another wave's MFMA runs, so
+    the launch can reach at most flops / max(valu_us, mfma_us) (fully
+    overlapped) and, with no overlap at all, flops / (valu_us + mfma_us)."""
+    f = committed_fields("mfma_busy", workload_name)
+    try:
+        valu_us = float(f["valu_bound_us_at_2400mhz"])
+        mfma_us = float(f["mfma_bound_us_at_2400mhz"])
+        insts = int(float(f["valu_non_mfma_insts"]))
+    except (TypeError, KeyError, ValueError):
+        return None
+    tf = flops / 1e12 / 1e-6
+    return {"valu_insts_per_launch": insts,
+            "valu_us_at_2400mhz": round(valu_us, 2),
+            "mfma_us_at_2400mhz": round(mfma_us, 2),
+            "frac_ceiling_overlapped": round(tf / max(valu_us, mfma_us) / peak, 4),
+            "frac_ceiling_serial": round(tf / (valu_us + mfma_us) / peak, 4)}
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed PMC summary, if it is current.
+
+    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each
+    scaled by the copy-kernel calibration factor) and the digest of the kernel
+    sources it was taken with; a changed kernel makes the figure stale (None).
+    """
+    f = committed_fields("hbm_traffic", workload_name)
+    try:
+        return None if f is None else float(f["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -209,8 +259,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # The GPU's clocks take about 30 ms of back-to-back launches to settle
-    # (about 100 launches of the causal 4096 workload); 200 warm-up steps
-    # put every timed step in the steady state.
+    # (about 100 launches of the causal 4096 workload); by default 200 warm-up
+    # steps put every timed step in the steady state.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="causal_bf16_b2h32n4096d128")
     ap.add_argument("--seed", type=int, default=1)
@@ -332,7 +382,20 @@ def main():
     torch.cuda.synchronize()
 
     wall, avg_launch_s = (timed_graph if args.graph else timed)(step, args.steps)
-    call_stream = stream  # the comparison runs below are eager
+    call_stream = stream  # the runs below are eager
+
+    # After the timed window: the same step once the clocks have settled.  The
+    # first ~100 launches of a cold GPU run at a lower clock (the cycle counts
+    # per launch stay flat), so a short warm-up puts the timed window inside
+    # that phase; this figure is reported beside `value`, never in its place.
+    before = args.warmup + args.steps
+    settle = max(0, STEADY_AFTER_LAUNCHES - before)
+    for _ in range(settle):
+        step()
+    _, steady_s = timed(step, max(args.steps, 50))
+    steady = {"kernel_us": round(steady_s * 1e6, 2),
+              "tflops": round(flops / steady_s / 1e12, 3),
+              "launches_before": before + settle}
 
     dense = None
     if sparse_mask is not None:  # after the timed region: every pair, on the same inputs
@@ -405,11 +468,14 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(w.name),
+            "mfma_busy": measured_mfma_busy(w.name),
+            **({"valu_bound": valu_bound(w.name, flops, peak)} if w.d <= 64 else {}),
             **({"kernels": "split forward + merge (one step, both launches)"}
                if splits else {}),
             **({"kernels": "row sums D + dK/dV + dQ (one step, three launches)"}
                if backward else {}),
         },
+        "steady": {**steady, "frac": round(flops / steady_s / 1e12 / peak, 4)},
         "cpu_baseline": None,
         **({"unsplit": unsplit} if splits else {}),
         **({"dense": dense} if sparse_mask is not None else {}),
