@@ -33,8 +33,32 @@ def test_summary_names_its_command(name):
     text = open(os.path.join(PROFILES, name)).read()
     cmd = [line for line in text.splitlines() if line.startswith("command")]
     assert cmd, f"{name}: no command line"
-    assert "rocprofv3" in cmd[0] and "bench.py" in cmd[0]
+    runs = [line for line in text.splitlines() if re.search(r"rocprofv3 --.* -- ", line)]
+    assert runs, f"{name}: no rocprofv3 command"
+    for line in runs:
+        assert "bench.py" in line
     assert "_work" not in text  # only committed files are run
+
+
+@pytest.mark.parametrize("name", [f for f in _summaries() if f.startswith("mfma_busy_")])
+def test_mfma_summary_is_consistent(name):
+    fields = {}
+    for line in open(os.path.join(PROFILES, name)):
+        m = re.match(r"^(\w+):\s*(\S+)$", line.strip())
+        if m:
+            fields[m.group(1)] = m.group(2)
+    for key in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU",
+                "SQ_INSTS_SALU", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "mfma_busy",
+                "valu_bound_us_at_2400mhz", "mfma_bound_us_at_2400mhz", "source_digest"):
+        assert key in fields, f"{name}: missing {key}"
+    busy = float(fields["SQ_VALU_MFMA_BUSY_CYCLES"])
+    # 8 XCDs, 1024 SIMDs
+    assert float(fields["mfma_busy"]) == pytest.approx(
+        busy / (float(fields["GRBM_GUI_ACTIVE"]) / 8 * 1024), abs=1e-4)
+    # a 32x32x16 bf16 MFMA is 64 MOPs of 512 flops and keeps its SIMD busy 32 cycles
+    mfma = float(fields["SQ_INSTS_MFMA"])
+    assert busy == pytest.approx(32 * mfma, rel=0.02)
+    assert float(fields["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) == pytest.approx(64 * mfma, rel=0.02)
 
 
 @pytest.mark.parametrize("name", [f for f in _summaries() if f.startswith("hbm_traffic_")])
