@@ -302,6 +302,29 @@ def test_workload_every_row(gpu_lib, w, seeds):
         assert el <= TOL_L
 
 
+@pytest.mark.parametrize("group", range(4))
+def test_long_every_row(gpu_lib, group):
+    """Every row of the N=16384 workload (seed 1) against the oracle, four of
+    its 16 heads per test: the oracle's float64 S of one head is 2 GiB and
+    takes several seconds, so the heads go one at a time on the host."""
+    w, seed = workloads.LONG_16K, SEEDS[0]
+    heads = range(4 * group, 4 * group + 4)
+    _say(f"[parity] every row: {w.describe()} seed={seed} heads {heads.start}..{heads.stop - 1}")
+    q, k, v = make_inputs(w, seed)
+    O, L = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    eo = el = 0.0
+    for h in heads:
+        sl = (slice(0, 1), slice(h, h + 1))
+        Or, Lr = oracle.attention(to_f64_numpy(q[sl]), to_f64_numpy(k[sl]), to_f64_numpy(v[sl]),
+                                  w.scale, w.causal)
+        eo = max(eo, float(np.abs(to_f64_numpy(O[sl]) - Or).max()))
+        el = max(el, float(np.abs(L[sl].cpu().double().numpy() - Lr).max()))
+    _say(f"[parity]   {len(heads) * w.N} rows: max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= TOL_O[w.dtype]
+    assert el <= TOL_L
+
+
 def test_deterministic(gpu_lib):
     _say("[parity] determinism")
     q, k, v = make_qkv(2, 4, 777, 128, torch.bfloat16, seed=4, device="cuda")
