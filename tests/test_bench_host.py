@@ -76,10 +76,13 @@ def test_traffic_summary_is_consistent(name):
     # FETCH_SIZE counts half of a plain copy's reads on this chip, WRITE_SIZE all
     # of its writes; the calibration copy fixes both factors.
     assert 1.5 < fetch_f < 2.5 and 0.8 < write_f < 1.2
-    kf = [float(x) for x in fields["kernel_fetch_kib_per_dispatch"].split()]
-    kw = [float(x) for x in fields["kernel_write_kib_per_dispatch"].split()]
-    fb = sum(kf) / len(kf) * 1024 * fetch_f
-    wb = sum(kw) / len(kw) * 1024 * write_f
+    # the per-launch figure is the median over the profiled dispatches
+    fb = float(fields["kernel_fetch_kib_median"]) * 1024 * fetch_f
+    wb = float(fields["kernel_write_kib_median"]) * 1024 * write_f
+    for key in ("kernel_fetch_kib_per_dispatch", "kernel_write_kib_per_dispatch"):
+        first = [float(x) for x in fields[key].split()]
+        median = float(fields[key.replace("per_dispatch", "median")])
+        assert all(abs(x - median) <= 0.05 * median for x in first), key
     # the factors are printed to 5 decimals: agree to 1e-5 relative
     assert fb == pytest.approx(float(fields["fetch_bytes_per_launch"]), rel=1e-5)
     assert wb == pytest.approx(float(fields["write_bytes_per_launch"]), rel=1e-5)
