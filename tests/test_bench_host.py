@@ -88,3 +88,45 @@ def test_traffic_summary_is_consistent(name):
     assert wb == pytest.approx(float(fields["write_bytes_per_launch"]), rel=1e-5)
     assert float(fields["traffic_bytes_per_launch"]) == pytest.approx(
         float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"]), abs=2)
+
+
+def _bench():
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def test_committed_fields_go_stale_with_the_sources(tmp_path, monkeypatch):
+    """A counter summary counts only while the kernel sources are the ones it
+    was taken with: another digest makes bench.py report null."""
+    bench = _bench()
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    text = ("mfma_busy: 0.5\nvalu_bound_us_at_2400mhz: 10.0\nmfma_bound_us_at_2400mhz: 20.0\n"
+            "valu_non_mfma_insts: 1000\ntraffic_bytes_per_launch: 123\n")
+    (tmp_path / "mfma_busy_w.txt").write_text(text + f"source_digest: {bench.kernel_source_digest()}\n")
+    (tmp_path / "hbm_traffic_w.txt").write_text(text + "source_digest: 0000000000000000\n")
+    assert bench.measured_mfma_busy("w") == 0.5
+    assert bench.measured_traffic("w") is None          # stale digest
+    assert bench.measured_mfma_busy("missing") is None  # no file
+
+
+def test_valu_bound_ceilings(tmp_path, monkeypatch):
+    """frac_ceiling_overlapped = flops / max(valu, mfma time) / peak and
+    frac_ceiling_serial = flops / (valu + mfma time) / peak."""
+    bench = _bench()
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    (tmp_path / "mfma_busy_w.txt").write_text(
+        "valu_bound_us_at_2400mhz: 30.0\nmfma_bound_us_at_2400mhz: 20.0\nvalu_non_mfma_insts: 7\n"
+        f"source_digest: {bench.kernel_source_digest()}\n")
+    peak = bench.PEAK_BF16_TFLOPS
+    flops = 20e-6 * peak * 1e12  # exactly 20 us at the peak
+    vb = bench.valu_bound("w", flops, peak)
+    assert vb["valu_insts_per_launch"] == 7
+    assert vb["frac_ceiling_overlapped"] == pytest.approx(20 / 30, abs=1e-4)
+    assert vb["frac_ceiling_serial"] == pytest.approx(20 / 50, abs=1e-4)
+
+
+def test_host_description_fields():
+    d = _bench().host_description()
+    assert set(d) == {"cpu_model", "affinity_cpus", "blas_threads"}
+    assert d["affinity_cpus"] == len(os.sched_getaffinity(0))
