@@ -461,6 +461,9 @@ def main():
                       if sparse_mask is not None else {}),
                    **({"num_splits": splits} if splits else {})},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        # the peak assumes 256 CUs at 2.4 GHz (the clock under load is in the
+        # committed counter summaries: GRBM_GUI_ACTIVE cycles over time)
+        "device": {"name": props.name, "cus": props.multi_processor_count},
         "roofline": {
             "bound": "alu" if w.dtype == "fp32" else "mfma",
             "achieved": round(achieved, 3),
