@@ -380,6 +380,35 @@ def test_long_sequence_extra_memory_is_linear(gpu_lib):
     assert peak <= expected + (1 << 20), (peak, expected)
 
 
+@pytest.mark.parametrize("case", [(262144, 128, False), (262144, 64, False), (131072, 128, True),
+                                  (262144 - 37, 64, True)],
+                         ids=lambda c: "n{}d{}-{}".format(c[0], c[1], "causal" if c[2] else "full"))
+def test_very_long_sequence_sampled(gpu_lib, case):
+    """One head at N up to 2^18 (the persistent launch under the causal mask,
+    512 or 1024 query tiles, a ragged tail in the last case): element offsets
+    far past those of the workloads, checked on sampled rows (tile edges,
+    the last rows, random rows) against the oracle row by row."""
+    N, d, causal = case
+    _say(f"[parity] very long N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(1, 1, N, d, torch.bfloat16, seed=N % 1000 + d)
+    O, L = gpu_lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+    rng = np.random.default_rng(N + d)
+    picks = {0, 63, 64, 255, 256, N // 2, N - 257, N - 256, N - 65, N - 64, N - 2, N - 1}
+    picks |= set(int(i) for i in rng.integers(0, N, size=52))
+    rows = [(0, 0, i) for i in sorted(picks)]
+    idx = torch.tensor(rows, dtype=torch.long)
+    Og = O[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+    Lg = L[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+    Or, Lr = oracle.attention_rows(to_f64_numpy(q), to_f64_numpy(k), to_f64_numpy(v),
+                                   1 / math.sqrt(d), causal, rows)
+    eo, el = np.abs(Og - Or).max(), np.abs(Lg - Lr).max()
+    _say(f"[parity]   rows={len(rows)} max|dO|={eo:.3e} max|dL|={el:.3e}")
+    assert eo <= TOL_O["bf16"]
+    assert el <= TOL_L
+
+
 def test_error_status_raises(gpu_lib):
     q = torch.zeros((1, 1, 8, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(gpu_lib.FaError) as ei:
