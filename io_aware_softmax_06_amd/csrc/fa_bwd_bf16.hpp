@@ -283,11 +283,22 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       // is free except for its V-style Q, and so is the P slot (the dK wave
       // read P_{t-1} before this barrier).
       wait_vmcnt<kPer>();
+      if (wave == 0) {
+        // The tile's L becomes the exponent offset -L log2(e) once, here,
+        // instead of in every dV lane for every element (-inf, a row that
+        // saw no key, stays -inf so that its probabilities are 0).
+        float* lt = reinterpret_cast<float*>(smem + (t & 1) * Lay::kStage + Lay::kOffL) + lane;
+        const float l = *lt;
+        *lt = l == kNegInf ? kNegInf : -l * kLog2e;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
       block_sync();
       if (t + 1 < nq) load_main(t + 1);
       const int q0 = t * kBN;
-      // A wave whose keys all lie after the tile's last query has nothing to do.
-      const bool active = kw0 < N && !(CAUSAL && q0 + kBN - 1 < kw0);
+      // A wave whose keys all lie after the tile's last query has nothing to do
+      // (the same in every lane: a scalar, so that the branches on it are).
+      const bool active =
+          __builtin_amdgcn_readfirstlane((kw0 < N && !(CAUSAL && q0 + kBN - 1 < kw0)) ? 1 : 0) != 0;
       const uint32_t st = smem_lds + (t & 1) * Lay::kStage;
       const char* stage = smem + (t & 1) * Lay::kStage;
 
@@ -298,9 +309,8 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         score_tile<D, T>(st + (DK ? Lay::kOffDok : Lay::kOffQk) + k_lane, bop, sacc);
         if constexpr (!DK) {
           // P = exp(scale S - L); the four queries of a group g are
-          // consecutive, so their L values come as one 16-byte read.
+          // consecutive, so their offsets -L log2(e) come as one 16-byte read.
           const float* Lt = reinterpret_cast<const float*>(stage + Lay::kOffL);
-          const bool need_mask = (q0 + kBN > N) || (CAUSAL && kw0 + 31 > q0);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -308,18 +318,25 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
               const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
               const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qoff);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int e = 4 * g + r;
-                // -inf for a row that saw no key makes its probabilities 0.
-                const float nl = l4[r] == kNegInf ? kNegInf : -l4[r] * kLog2e;
-                float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
-                if (need_mask) {
-                  const int q = q0 + qoff + r;
-                  if (q >= N || (CAUSAL && key > q)) p = 0.f;
-                }
-                sacc[kb][e] = p;
-              }
+              for (int r = 0; r < 4; ++r)
+                sacc[kb][4 * g + r] =
+                    fast_exp2(__builtin_fmaf(sacc[kb][4 * g + r], scale_log2, l4[r]));
             }
+          // Only tiles on the diagonal or past N need the mask (a scalar branch).
+          const bool need_mask =
+              __builtin_amdgcn_readfirstlane(((q0 + kBN > N) || (CAUSAL && kw0 + 31 > q0)) ? 1 : 0) != 0;
+          if (need_mask) {
+            // (kept a real branch: without it the masking is folded into
+            // selects that every tile pays for)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int q = q0 + 32 * kb + 16 * (e >> 3) + 8 * hh + 4 * ((e >> 2) & 1) + (e & 3);
+                if (q >= N || (CAUSAL && key > q)) sacc[kb][e] = 0.f;
+              }
+          }
           to_b_operand<T>(sacc, bf);
           // P goes to the dK wave as float16 whatever the input type: P <= 1,
           // and float16 keeps 11 bits of it (bfloat16 8), so dS loses nothing
