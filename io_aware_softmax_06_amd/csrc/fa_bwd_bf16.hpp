@@ -447,6 +447,7 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   int my_tiles = 0;
   if (wq0 < N) my_tiles = ((CAUSAL ? min(N, wq0 + 32) : N) + kBN - 1) / kBN;
+  my_tiles = __builtin_amdgcn_readfirstlane(my_tiles);  // the same in every lane
 
   // Q^T and dO^T as B operands (one query per lane); this row's L and D.
   V8 qf[D / 16], dof[D / 16];
@@ -497,18 +498,28 @@ fa_bwd_dq_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     f32x16 sacc[2], dpacc[2];
     score_tile<D, T>(st + Lay::kOffKk + k_lane, qf, sacc);
     score_tile<D, T>(st + Lay::kOffVk + k_lane, dof, dpacc);
-    const bool need_mask = (kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
-        if (need_mask) {
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, nl));
+    // Only tiles on the diagonal or past N need the mask: a scalar branch
+    // (kept a real one, not folded into selects that every tile would pay).
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+                               ((kv0 + kBN > N) || (CAUSAL && kv0 + kBN - 1 > wq0)) ? 1 : 0) != 0;
+    if (need_mask) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
           const int kk = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hh + (e & 3));
-          if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+          if (kk >= N || (CAUSAL && kk > qrow)) sacc[kb][e] = 0.f;
         }
-        dpacc[kb][e] = p * (dpacc[kb][e] - dq_row);
-      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dpacc[kb][e] = sacc[kb][e] * (dpacc[kb][e] - dq_row);
     V8 dsf[kBN / 16];
     to_b_operand<T>(dpacc, dsf);
     // dQ^T += K^T dS^T (K read transposed from its V-style copy).
