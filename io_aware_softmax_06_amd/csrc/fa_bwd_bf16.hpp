@@ -119,6 +119,19 @@ __device__ __forceinline__ void store_rows(uint16_t* __restrict__ out_row, const
     }
 }
 
+// p * t with p a float16 taken from the low (H = 0) or high (H = 1) half of a
+// packed pair and t a float32: one v_fma_mix_f32 (p converted exactly, plus
+// 0) instead of a conversion and a multiply.
+template <int H>
+__device__ __forceinline__ float mul_f16_f32(uint32_t p2, float t) {
+  float r;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(p2), "v"(t));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(p2), "v"(t));
+  return r;
+}
+
 // 64 floats (one per row of a tile) straight into LDS; rows past the end of
 // the resource read as 0.  Issued by one wave.
 __device__ __forceinline__ void load_row_floats(char* smem, int off, __amdgpu_buffer_rsrc_t rsrc,
@@ -368,9 +381,9 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       if constexpr (DK) {
         // dS = P (dP - D), with P from the dV wave (float16).
         const float* Dt = reinterpret_cast<const float*>(stage + Lay::kOffD);
-        f16x8 pp[kBN / 16];
+        u32x4 pp[kBN / 16];  // eight float16 per 16-key step, as four packed pairs
 #pragma unroll
-        for (int s2 = 0; s2 < kBN / 16; ++s2) pp[s2] = __builtin_bit_cast(f16x8, p_slot[64 * s2]);
+        for (int s2 = 0; s2 < kBN / 16; ++s2) pp[s2] = p_slot[64 * s2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -378,10 +391,11 @@ fa_bwd_dkdv_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             const int qoff = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qoff);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 4 * g + r;
-              const float p = (float)pp[2 * kb + (e >> 3)][e & 7];
-              sacc[kb][e] = p * (sacc[kb][e] - d4[r]);
+            for (int r = 0; r < 4; r += 2) {
+              const int e = 4 * g + r;  // elements e, e + 1: one packed pair of P
+              const uint32_t p2 = pp[2 * kb + (e >> 3)][(e & 7) >> 1];
+              sacc[kb][e] = mul_f16_f32<0>(p2, sacc[kb][e] - d4[r]);
+              sacc[kb][e + 1] = mul_f16_f32<1>(p2, sacc[kb][e + 1] - d4[r + 1]);
             }
           }
         to_b_operand<T>(sacc, bf);
