@@ -36,8 +36,9 @@ launch stream) to the dense bf16 MFMA peak, with the MFMA-busy fraction and
 HBM bytes of the committed counter summaries (null once the kernel sources
 have changed since they were taken) and, for d <= 64, the VALU-issue bound.
 `steady` times the same step again after the timed window, once at least 300
-launches have run: with a short --warmup the timed window falls in the GPU's
-slower first ~100 launches, and the two figures then differ.  `cpu_baseline` times the float64
+launches and 0.1 s of back-to-back launches have run: with a short --warmup the
+timed window falls in the GPU's slower first ~30 ms, and the two figures then
+differ.  `cpu_baseline` times the float64
 CPU oracle on a bounded sample of the same workload (whole heads, ~10 s).
 """
 
@@ -58,9 +59,11 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) + % of bf16 MFMA peak, 1×MI35
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_F32_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
-# Launches after which the GPU clock has settled (the slow start lasts about
-# 100 launches of the causal N=4096 workload, ~30 ms).
+# Load after which the GPU clock has settled: the slow start lasts about 100
+# launches (~30 ms) of the causal N=4096 workload; short kernels need more
+# launches for the same time (the N=1024 d=64 workload: ~2000, ~50 ms).
 STEADY_AFTER_LAUNCHES = 300
+STEADY_AFTER_SECONDS = 0.1
 CSRC = os.path.join(ROOT, "io_aware_softmax_06_amd", "csrc")
 
 
@@ -377,6 +380,7 @@ def main():
         wall_s = time.perf_counter() - t0
         return wall_s, start.elapsed_time(end) / 1e3 / n
 
+    t_load = time.perf_counter()  # start of back-to-back launches (for `steady`)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -389,9 +393,12 @@ def main():
     # per launch stay flat), so a short warm-up puts the timed window inside
     # that phase; this figure is reported beside `value`, never in its place.
     before = args.warmup + args.steps
-    settle = max(0, STEADY_AFTER_LAUNCHES - before)
-    for _ in range(settle):
-        step()
+    settle = 0
+    while before + settle < STEADY_AFTER_LAUNCHES or time.perf_counter() - t_load < STEADY_AFTER_SECONDS:
+        for _ in range(50):
+            step()
+        settle += 50
+        torch.cuda.synchronize()
     _, steady_s = timed(step, max(args.steps, 50))
     steady = {"kernel_us": round(steady_s * 1e6, 2),
               "tflops": round(flops / steady_s / 1e12, 3),
