@@ -219,7 +219,8 @@ int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, flo
  *                    row), overwritten; nothing needs clearing before.
  *   workspace_bytes  size of the workspace buffer.
  * fa_bwd_workspace returns that size in bytes (4 * B * H * N), or a negative
- * fa_status (FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D) for arguments fa_bwd rejects.
+ * fa_status (FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D) for arguments fa_bwd rejects;
+ * FA_ERR_SHAPE also when 4 * B * H * N does not fit a signed 64-bit size.
  *
  * Every buffer lives in device memory of the current device and stays owned
  * by the caller.  Three kernels are enqueued on `stream` (D, then dK and dV,
