@@ -43,10 +43,11 @@
 //    runs on from one tile to the next, so that the next tile's first K and V
 //    tiles load under the current tile's last iterations.
 //  * The reference point of the online softmax moves only when a row's maximum
-//    grows by more than 2^8 (in base-2 units); until then probabilities are
-//    taken against the stale reference and are at most 2^8, which fp32 and
-//    bf16 hold exactly as well.  Softmax is invariant to the shift, so this is
-//    the same result while skipping almost every rescale of the output.
+//    grows by more than 8 (in base-2 units); until then probabilities are
+//    taken against the stale reference and are at most 2^8 (2^16 on tiles
+//    that skip the row maximum, see FastState), which fp32 and bf16 hold as
+//    well.  Softmax is invariant to the shift, so this is the same result
+//    while skipping almost every rescale of the output.
 //  * Scores are scaled by scale*log2(e) inside one FMA and exponentiated with
 //    v_exp_f32 (base 2); L is formed in natural-log units at the end.
 #pragma once
@@ -852,11 +853,14 @@ fa_fwd_bf16_kernel(
     // exponentiated against the current reference right away: the row
     // maximum, its half-wave exchange and the reference update are skipped.
     // The raw scores are kept, and the tile's half-row sums of the
-    // probabilities are checked at the end: if one exceeds kFastLimit (some
-    // probability above it, which the reference rule would have moved), the
-    // tile is redone along the path with the maximum, and the wave returns to
-    // that path for the next tile.  Otherwise the result is the one the
-    // reference rule gives: the same reference, the same probabilities.
+    // probabilities are checked at the end: if one exceeds kFastLimit, the
+    // tile is redone along the path with the maximum (which moves the
+    // reference), and the wave returns to that path for the next tile.
+    // Otherwise every probability of the tile is at most kFastLimit (they
+    // are non-negative and their sum is): the reference may lag the row
+    // maximum by up to 16 instead of kTau (base 2), which float32 sums and
+    // 16-bit P hold with room to spare, and by shift invariance the
+    // normalised result is the same softmax.
     constexpr float kFastLimit = 65536.f;  // 2^16
     struct FastState {
       float l, lh;   // this tile's sums of the float32 and of the rounded probabilities
