@@ -34,7 +34,7 @@ count 4*B*H*N^2*d (halved for causal) over the timed steps' wall time.
 `roofline` relates the kernel's average launch duration (HIP events on the
 launch stream) to the dense bf16 MFMA peak, with the MFMA-busy fraction and
 HBM bytes of the committed counter summaries (null once the kernel sources
-have changed since they were taken) and, for d <= 64, the VALU-issue bound.
+have changed since they were taken) and, for d <= 64, the VALU bound.
 `steady` times the same step again after the timed window, once at least 300
 launches and 0.1 s of back-to-back launches have run: with a short --warmup the
 timed window falls in the GPU's slower first ~30 ms, and the two figures then
@@ -126,10 +126,11 @@ def measured_mfma_busy(workload_name):
 
 
 def valu_bound(workload_name, flops, peak):
-    """The VALU-issue bound of one launch from the committed counters (None if
+    """The VALU bound of one launch from the committed counters (None if
     stale).  The non-MFMA VALU instructions of the dispatch, spread evenly
-    over the 1024 SIMDs at the issue costs measured for this kernel's mix,
-    give `valu_us` at the 2.4 GHz peak clock; the MFMA work gives `mfma_us`.
+    over the 1024 SIMDs at the throughputs measured with four waves per SIMD
+    (10.4 cycles per exponential, 4.7 per other wave64 instruction), give
+    `valu_us` at the 2.4 GHz peak clock; the MFMA work gives `mfma_us`.
     A SIMD issues VALU work of one wave while another wave's MFMA runs, so
     the launch can reach at most flops / max(valu_us, mfma_us) (fully
     overlapped) and, with no overlap at all, flops / (valu_us + mfma_us)."""
