@@ -128,12 +128,14 @@ def measured_mfma_busy(workload_name):
 def valu_bound(workload_name, flops, peak):
     """The VALU bound of one launch from the committed counters (None if
     stale).  The non-MFMA VALU instructions of the dispatch, spread evenly
-    over the 1024 SIMDs at the throughputs measured with four waves per SIMD
-    (10.4 cycles per exponential, 4.7 per other wave64 instruction), give
-    `valu_us` at the 2.4 GHz peak clock; the MFMA work gives `mfma_us`.
-    A SIMD issues VALU work of one wave while another wave's MFMA runs, so
-    the launch can reach at most flops / max(valu_us, mfma_us) (fully
-    overlapped) and, with no overlap at all, flops / (valu_us + mfma_us)."""
+    over the 1024 SIMDs at the throughputs measured with two waves per SIMD
+    and one workgroup per CU (9.8 SIMD cycles per exponential, 2.9 per other
+    wave64 instruction: the cheapest, fma/add/mul, so that this is a lower
+    bound), give `valu_us` at the 2.4 GHz peak clock; the MFMA work gives
+    `mfma_us`.  A SIMD issues VALU work of one wave while another wave's
+    MFMA runs, so the launch can reach at most flops / max(valu_us, mfma_us)
+    (fully overlapped) and, with no overlap at all, flops / (valu_us +
+    mfma_us)."""
     f = committed_fields("mfma_busy", workload_name)
     try:
         valu_us = float(f["valu_bound_us_at_2400mhz"])

@@ -59,6 +59,13 @@ def test_mfma_summary_is_consistent(name):
     mfma = float(fields["SQ_INSTS_MFMA"])
     assert busy == pytest.approx(32 * mfma, rel=0.02)
     assert float(fields["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) == pytest.approx(64 * mfma, rel=0.02)
+    # the VALU issue bound: per-instruction costs spread over the 1024 SIMDs, at 2.4 GHz
+    trans = float(fields["SQ_INSTS_VALU_TRANS_F32"])
+    other = float(fields["SQ_INSTS_VALU"]) - mfma - trans
+    cyc = (float(fields["valu_cost_trans_cycles"]) * trans
+           + float(fields["valu_cost_other_cycles"]) * other) / 1024
+    assert float(fields["valu_issue_cycles_per_simd"]) == pytest.approx(cyc, rel=1e-3)
+    assert float(fields["valu_bound_us_at_2400mhz"]) == pytest.approx(cyc / 2400, rel=1e-3)
 
 
 @pytest.mark.parametrize("name", [f for f in _summaries() if f.startswith("hbm_traffic_")])
